@@ -1,0 +1,76 @@
+"""One round composed from the oracle's steps (test infrastructure only).
+
+Order within a round (Graft page, section 2; section 6, second level):
+the previous round's verified positions update the successor table, the
+current token's retrieval tree is read from the updated table, the hybrid
+tree is built and flattened, the target verifies it (tree attention, then
+the lm-head), every position's top-k is taken, and the deepest greedily
+accepted path is kept.  The next round's update reads this round's tokens
+and top-k.
+
+The inputs object only needs the attributes named below (numpy arrays);
+hidden states are passed in because the synthetic target model plants them
+on the built tree.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import accept as _accept
+from . import attention as _attention
+from . import lmhead as _lmhead
+from . import table as _table
+from . import template as _template
+from . import topk as _topk
+from . import tree as _tree
+
+
+def tree_stage(ri, dmax: int = 8):
+    """Update + retrieve + build.  Returns dict(table, tparent, trank,
+    tmpl_off, ret_token, tree)."""
+    table = _table.update(ri.table, ri.prev_n, ri.prev_row_off, ri.prev_token, ri.prev_topk)
+    tp_all, tr_all, rt_all, off = [], [], [], [0]
+    for b in range(ri.B):
+        tp, tr, _ = _template.template(int(ri.n_ret[b]), ri.k, dmax)
+        rt = _table.retrieve(table, int(ri.root_token[b]), tp, tr)
+        tp_all += tp
+        tr_all += tr
+        rt_all += rt
+        off.append(off[-1] + len(tp))
+    tparent = np.array(tp_all, np.int32)
+    trank = np.array(tr_all, np.int32)
+    ret_token = np.array(rt_all, np.int32)
+    tmpl_off = np.array(off, np.int32)
+    wl = ri.wl
+    tree = _tree.build_batch(ri.cand_parent, ri.cand_token, ri.cand_score, ri.cand_off,
+                             ri.budget, ret_token, tparent, tmpl_off, ri.ctx_len, ri.V,
+                             ri.row_off, static_replace=wl.static_replace, table=table,
+                             replace_thresh=wl.replace_thresh)
+    return dict(table=table, tparent=tparent, trank=trank, tmpl_off=tmpl_off,
+                ret_token=ret_token, tree=tree)
+
+
+def kv_f64(ri, b: int):
+    """Request b's K and V caches as fp64 [Hkv, ctx_b + N, d]."""
+    L = int(ri.ctx_len[b]) + ri.N
+    K = _lmhead.bf16_to_f64(ri.kcache[b, :, :L]).reshape(ri.wl.Hkv, L, ri.wl.d)
+    V = _lmhead.bf16_to_f64(ri.vcache[b, :, :L]).reshape(ri.wl.Hkv, L, ri.wl.d)
+    return K, V
+
+
+def verify_stage(ri, tree, hidden_bits, w_bits, attention_nodes=None):
+    """Tree attention (one layer), lm-head, top-k, acceptance."""
+    q = _lmhead.bf16_to_f64(ri.q).reshape(ri.q.shape)
+    Ks, Vs = [], []
+    for b in range(ri.B):
+        K, V = kv_f64(ri, b)
+        Ks.append(K)
+        Vs.append(V)
+    att = _attention.tree_attention(q, Ks, Vs, ri.ctx_len, tree["n"], ri.row_off,
+                                    tree["mask"], ri.scale, nodes=attention_nodes)
+    logits = _lmhead.logits(hidden_bits, w_bits)
+    ids, vals = _topk.topk(logits, ri.k)
+    lens, paths, bonus = _accept.accept_batch(tree["n"], ri.row_off, tree["parent"],
+                                              tree["token"], ids[:, 0])
+    return dict(attention=att, logits=logits, topk_id=ids, topk_val=vals,
+                acc_len=lens, acc_path=paths, bonus=bonus)
