@@ -1,0 +1,32 @@
+// Shared host/device helpers of libgraft (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "graft.h"
+
+namespace graft {
+
+// Records a printf-style message for graft_last_error() and returns `code`.
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+// Returns GRAFT_OK, or GRAFT_EHIP with the HIP error text if the last launch failed.
+int check_launch(const char *what);
+void clear_error();
+
+inline hipStream_t as_stream(graft_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ORs error bits into the caller's device flag word (vector-memory atomic).
+__device__ inline void raise_flag(int32_t *err, int bits) {
+  if (err) atomicOr(err, bits);
+}
+
+// (value, id) ordering used by every ranking: larger value first, ties to
+// the lower id.  NaN never ranks above anything.
+__device__ inline bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+}  // namespace graft

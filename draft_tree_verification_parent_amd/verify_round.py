@@ -1,0 +1,171 @@
+"""One round of tree speculative decoding driven through libgraft.
+
+Order on one HIP stream (Graft page, arXiv:2605.20104 write-up, section 2;
+section 6, second level):
+  1. graft_table_update_retrieve -- the previous round's verified positions
+     rewrite their table rows, then the retrieval template is expanded from
+     the current root token;
+  2. graft_build_tree            -- select, append retrieved nodes, flatten,
+                                    depth / positions / mask;
+  3. graft_tree_attention        -- one tree-masked attention layer;
+  4. graft_lmhead_topk           -- logits (materialised) ...
+  5. graft_lmhead_topk           -- ... and their per-row top-k;
+  6. graft_accept                -- deepest accepted path and bonus token.
+The next round's update reads this round's tree tokens and top-k ids.
+
+Device memory comes from torch; every computation runs in libgraft.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import api
+from ._native import TREE_PRUNE, TREE_STATIC_REPLACE
+
+STEPS = ("update_retrieve", "build_tree", "tree_attention", "lmhead", "topk", "accept")
+
+
+def _i32(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
+
+
+def _bf16(bits, dev):
+    a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(a).to(dev).view(torch.bfloat16)
+
+
+class VerifyRound:
+    def __init__(self, ri, w_bits=None, device="cuda", dmax: int = 8):
+        dev = torch.device(device)
+        wl = ri.wl
+        self.ri, self.wl, self.dev = ri, wl, dev
+        B, N, k, V = ri.B, ri.N, ri.k, ri.V
+        self.B, self.N, self.k, self.V = B, N, k, V
+        self.rows = int(ri.row_off[-1])
+
+        # retrieval templates from the library's host helper
+        tp, tr, off = [], [], [0]
+        for b in range(B):
+            p, r = api.graft_make_template(int(ri.n_ret[b]), k, dmax)
+            tp.append(p)
+            tr.append(r)
+            off.append(off[-1] + len(p))
+        self.tmpl_rows = off[-1]
+        self.tmpl_parent = _i32(np.concatenate(tp) if self.tmpl_rows else np.zeros(1), dev)
+        self.tmpl_rank = _i32(np.concatenate(tr) if self.tmpl_rows else np.zeros(1), dev)
+        self.tmpl_off = _i32(off, dev)
+
+        self.table = _i32(ri.table, dev)
+        self.cand_parent = _i32(ri.cand_parent, dev)
+        self.cand_token = _i32(ri.cand_token, dev)
+        self.cand_score = torch.from_numpy(np.ascontiguousarray(ri.cand_score, np.float32)).to(dev)
+        self.cand_off = _i32(ri.cand_off, dev)
+        self.max_cand = int(np.max(np.diff(ri.cand_off)))
+        self.budget = _i32(ri.budget, dev)
+        self.ctx_len = _i32(ri.ctx_len, dev)
+        self.max_ctx = int(np.max(ri.ctx_len))
+        self.row_off = _i32(ri.row_off, dev)
+        self.root_token = _i32(ri.root_token, dev)
+        self.mode = TREE_STATIC_REPLACE if wl.static_replace else TREE_PRUNE
+
+        # the update list of the first round: the synthetic previous round
+        self.upd = dict(n=_i32(ri.prev_n, dev), row_off=_i32(ri.prev_row_off, dev),
+                        token=_i32(ri.prev_token, dev), topk=_i32(ri.prev_topk, dev),
+                        rows=int(ri.prev_row_off[-1]))
+
+        rows = self.rows
+        z = lambda *s, dt=torch.int32: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
+        self.ret_token = z(max(self.tmpl_rows, 1))
+        self.n_out = z(B)
+        self.parent = z(rows)
+        self.token = z(rows)
+        self.depth = z(rows)
+        self.pos = z(rows)
+        self.mask = z(rows, dt=torch.int64)
+        self.src = z(rows, dt=torch.int8)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        self.q = _bf16(ri.q.reshape(rows, wl.Hq, wl.d), dev)
+        self.kcache = _bf16(ri.kcache.reshape(-1), dev)
+        self.vcache = _bf16(ri.vcache.reshape(-1), dev)
+        self.kv_off = torch.from_numpy(np.ascontiguousarray(ri.kv_off, np.int64)).to(dev)
+        self.attn_out = torch.empty(rows, wl.Hq, wl.d, dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty(rows, wl.Hq, dtype=torch.float32, device=dev)
+        wsb = api.graft_tree_attention_workspace_bytes(B, wl.Hq, wl.Hkv, wl.d, self.max_ctx, N)
+        self.attn_ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+        self.w = _bf16(w_bits, dev) if w_bits is not None else None
+        self.hidden = None
+        self.logits = torch.empty(rows, V, dtype=torch.float32, device=dev)
+        self.topk_id = z(rows, k)
+        self.topk_val = torch.empty(rows, k, dtype=torch.float32, device=dev)
+        tkb = api.graft_lmhead_topk_workspace_bytes(rows, V, k)
+        self.topk_ws = torch.empty(max(tkb, 1), dtype=torch.uint8, device=dev)
+
+        self.acc_len = z(B)
+        self.acc_path = z(B, 64)
+        self.bonus = z(B)
+
+    def set_hidden(self, hidden_bits):
+        self.hidden = _bf16(hidden_bits.reshape(self.rows, self.wl.H), self.dev)
+
+    def chain_update(self):
+        """Make the next round's update read this round's verified nodes."""
+        self.upd = dict(n=self.n_out, row_off=self.row_off, token=self.token, topk=self.topk_id,
+                        rows=self.rows)
+
+    # individual steps -------------------------------------------------
+    def step_update_retrieve(self):
+        u = self.upd
+        api.graft_table_update_retrieve(self.table, u["n"], u["row_off"], u["rows"], u["token"],
+                                        u["topk"], self.root_token, self.tmpl_parent, self.tmpl_rank,
+                                        self.tmpl_off, self.tmpl_rows, self.ret_token, self.err)
+
+    def step_build_tree(self):
+        api.graft_build_tree(self.mode, self.cand_parent, self.cand_token, self.cand_score,
+                             self.cand_off, self.max_cand, self.budget, self.ret_token,
+                             self.tmpl_parent, self.tmpl_off if self.tmpl_rows else None,
+                             self.table, self.V, self.k, self.wl.replace_thresh, self.ctx_len,
+                             self.row_off, self.n_out, self.parent, self.token, self.depth,
+                             self.pos, self.mask, self.src, self.err)
+
+    def step_tree_attention(self):
+        wl = self.wl
+        api.graft_tree_attention(wl.Hq, wl.Hkv, wl.d, self.ri.scale, self.q, self.kcache, self.vcache,
+                                 self.kv_off, self.ri.kv_head_stride, self.ctx_len, self.max_ctx,
+                                 self.n_out, self.N, self.row_off, self.mask, self.attn_out, self.lse,
+                                 self.attn_ws, self.err)
+
+    def step_lmhead(self):
+        api.graft_lmhead_topk(self.rows, self.wl.H, self.V, 0, self.hidden, self.w, self.logits)
+
+    def step_topk(self):
+        api.graft_lmhead_topk(self.rows, self.wl.H, self.V, self.k, None, None, self.logits,
+                              self.topk_id, self.topk_val, self.topk_ws)
+
+    def step_accept(self):
+        api.graft_accept(self.n_out, self.row_off, self.parent, self.token, self.topk_id, self.k,
+                         self.acc_len, self.acc_path, self.bonus, self.err)
+
+    def run(self, events=None):
+        """Enqueue one round.  `events`, if given, is a dict step -> list that
+        receives (start, end) torch.cuda.Event pairs recorded on the stream."""
+        for name in STEPS:
+            fn = getattr(self, "step_" + name)
+            if events is None:
+                fn()
+            else:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                events.setdefault(name, []).append((e0, e1))
+
+    def tree_host(self):
+        """Built tree copied to the host (synchronises)."""
+        return dict(n=self.n_out.cpu().numpy(), parent=self.parent.cpu().numpy(),
+                    token=self.token.cpu().numpy(), depth=self.depth.cpu().numpy(),
+                    pos=self.pos.cpu().numpy(), mask=self.mask.cpu().numpy().view(np.uint64),
+                    src=self.src.cpu().numpy())

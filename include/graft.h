@@ -1,0 +1,259 @@
+/*
+ * graft.h -- C ABI of libgraft: one round of tree speculative decoding on
+ * an AMD Instinct MI355X (gfx950).
+ *
+ * A round (Graft page = write-up of arXiv:2605.20104, section 2; TreeGraft
+ * page = reading notes on arXiv:2608.26112, section 3):
+ *   graft_table_update_retrieve  previous round's verified positions rewrite
+ *                                their successor-table rows; the current
+ *                                token's retrieval template is expanded
+ *   graft_build_tree             draft selection + retrieved nodes, flatten,
+ *                                depth / positions / ancestor mask
+ *   graft_tree_attention         tree-masked GQA attention over the KV cache
+ *   graft_lmhead_topk            logits = hidden . W^T and per-row top-k
+ *   graft_accept                 deepest greedily accepted path + bonus token
+ *
+ * Conventions shared by every entry point
+ *  - Pointers marked (device) are device memory owned by the caller; the
+ *    library never allocates, frees or keeps them.  (host) pointers are
+ *    read or written before the call returns.
+ *  - Every device entry point is asynchronous on `stream` (a hipStream_t
+ *    passed as void*; NULL = the null stream) and never synchronises with
+ *    the host.
+ *  - Return value: GRAFT_OK, or a negative status when a host-checkable
+ *    argument is wrong (nothing is launched) or a launch failed;
+ *    graft_last_error() then describes it (per thread).
+ *  - Data-dependent faults found on the device (a token outside [0, V), a
+ *    parent that does not precede its child, ...) never cause an
+ *    out-of-bounds access: the kernel ORs a GRAFT_ERR_* bit into *err_flag
+ *    (device int32, may be NULL) and produces in-bounds but unspecified
+ *    values for the affected request.  The caller clears *err_flag.
+ *  - Tree batches use a padded row layout: request b owns rows
+ *    row_off[b] .. row_off[b+1]-1 (capacity <= 64) of every per-node array,
+ *    and its node i (i < n[b]) is row row_off[b] + i.  row_off is
+ *    non-decreasing.  Parent indices are request-local (root = node 0,
+ *    parent -1).
+ *  - Integer results are exact; ties in any ranking go to the lower index.
+ *  - bf16 tensors are raw bfloat16 bit patterns (uint16).
+ */
+#ifndef GRAFT_H
+#define GRAFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t graft_bf16;
+typedef void *graft_stream;
+
+#define GRAFT_MAX_NODES 64
+#define GRAFT_MAX_K 16
+#define GRAFT_MAX_CAND 2048
+#define GRAFT_MAX_UPDATE_ROWS 4096
+#define GRAFT_MAX_TEMPLATE_ROWS 4096
+
+/* return status */
+#define GRAFT_OK 0
+#define GRAFT_EINVAL (-1)       /* bad argument / shape; nothing launched */
+#define GRAFT_EUNSUPPORTED (-2) /* valid but not built (e.g. head dim 96) */
+#define GRAFT_EHIP (-3)         /* a HIP launch failed */
+
+/* device error-flag bits */
+#define GRAFT_ERR_TOKEN 1      /* token or successor id outside [0, V) */
+#define GRAFT_ERR_PARENT 2     /* parent not earlier than its child / no root */
+#define GRAFT_ERR_NOT_CLOSED 4 /* a kept draft node's parent was pruned */
+#define GRAFT_ERR_CAPACITY 8   /* tree larger than its rows or 64 nodes, or a
+                                  length above the bound given to the call */
+#define GRAFT_ERR_RANK 16      /* template rank outside [0, k) */
+
+/* node source codes written by graft_build_tree */
+#define GRAFT_SRC_ROOT 0
+#define GRAFT_SRC_DRAFT 1
+#define GRAFT_SRC_RETRIEVED 2
+#define GRAFT_SRC_REPLACED 3
+
+/* graft_build_tree modes */
+#define GRAFT_TREE_PRUNE 0          /* top-budget draft nodes + retrieved nodes */
+#define GRAFT_TREE_STATIC_REPLACE 1 /* top-budget draft nodes, low-score ones
+                                       swapped for table successors */
+
+const char *graft_last_error(void);
+int graft_version(void);
+
+/*
+ * Successor-table update, then template retrieval.
+ * Graft page, section 2 (second step: a GPU-resident table whose row t
+ * lists t's most likely successors; retrieval expands a stage-adaptive
+ * template from the current token by row lookups) and section 2 third step
+ * plus section 6 (every verified position, accepted or rejected, rewrites
+ * its token's row with the target's most likely successors).
+ *
+ * table       (device) int32 [V, k], updated in place.
+ * Update: the verified nodes of B_upd requests in the padded row layout
+ *   (upd_n [B_upd], upd_row_off [B_upd+1], device); upd_token [rows] and
+ *   upd_topk [rows, k] (device, row-major, the top-k ids of each row).  For
+ *   node r the whole row table[upd_token[r]] becomes upd_topk[r]; when
+ *   several nodes carry the same token the largest row index wins.
+ *   upd_rows (host) = upd_row_off[B_upd] <= GRAFT_MAX_UPDATE_ROWS.
+ *   A node whose token or ids fall outside [0, V) is skipped (ERR_TOKEN).
+ * Retrieval (after the update): request b's template nodes are
+ *   tmpl_off[b] .. tmpl_off[b+1]-1 (device) with request-local template
+ *   parents tmpl_parent (-1 = the root, otherwise an earlier node) and ranks
+ *   tmpl_rank in [0, k); node t gets
+ *     ret_token[t] = table'[token of its parent (root_token[b] for -1)][rank]
+ *   where table' is the updated table.  tmpl_rows (host) = tmpl_off[B] <=
+ *   GRAFT_MAX_TEMPLATE_ROWS.  Invalid links yield ret_token = -1 with
+ *   ERR_PARENT / ERR_RANK / ERR_TOKEN.
+ * Either part may be empty (B_upd = 0 or upd_rows = 0; B = 0 or
+ * tmpl_rows = 0).  One workgroup; calls that overlap on a table race.
+ */
+int graft_table_update_retrieve(int32_t *table, int V, int k,
+                                int B_upd, const int32_t *upd_n, const int32_t *upd_row_off,
+                                int upd_rows, const int32_t *upd_token, const int32_t *upd_topk,
+                                int B, const int32_t *root_token, const int32_t *tmpl_parent,
+                                const int32_t *tmpl_rank, const int32_t *tmpl_off, int tmpl_rows,
+                                int32_t *ret_token, int32_t *err_flag, graft_stream stream);
+
+/*
+ * Tree construction and flattening for B requests.
+ * Draft selection by cumulative score and global prune (TreeGraft page,
+ * section 3 and section 4 "How"); Graft's stage budgets and retrieval fill
+ * (Graft page, section 2, second step); flatten + tree positions + mask
+ * (Graft page, section 2, third step); static-tree replacement for batched
+ * serving (Graft page, section 4, serving paragraph).
+ *
+ * Candidates of request b: cand_off[b] .. cand_off[b+1]-1 (device) of
+ *   cand_parent (request-local, candidate 0 is the root with parent -1,
+ *   others point to an earlier candidate), cand_token, cand_score (fp32
+ *   cumulative score, non-increasing along paths).  max_cand (host) bounds
+ *   every request's candidate count, <= GRAFT_MAX_CAND.
+ * budget[b] (device): draft nodes kept, root included: the root plus the
+ *   budget-1 best other candidates by (score desc, index asc).
+ * mode GRAFT_TREE_PRUNE: the request's retrieved nodes ret_off[b] ..
+ *   ret_off[b+1]-1 (ret_token, ret_parent = template parents, -1 = root)
+ *   are appended after the kept draft nodes.  ret_* may be NULL for none.
+ * mode GRAFT_TREE_STATIC_REPLACE: no retrieved nodes; a kept draft node
+ *   with score < replace_thresh that is the j-th (0-based, by index) such
+ *   child of its parent takes token table[token(parent)][j] when j < k
+ *   (parent token after its own replacement), source GRAFT_SRC_REPLACED.
+ *   table (device int32 [V, k]) is read only in this mode.
+ * Output per request (device, padded row layout given by row_off [B+1]):
+ *   n_out[b]; parent, token, depth, pos = ctx_len[b] + depth (int32),
+ *   mask (uint64: bit j set iff node j is the node or its ancestor) and
+ *   src (int8).  Flattened order: kept draft nodes in ascending candidate
+ *   index, then retrieved nodes in template order.  Rows past n_out[b]
+ *   get parent = token = depth = pos = -1, mask = 0, src = -1.
+ * A tree over min(64, capacity) nodes, or over max_cand candidates, gives
+ * n_out[b] = 0 and ERR_CAPACITY.
+ */
+int graft_build_tree(int B, int mode,
+                     const int32_t *cand_parent, const int32_t *cand_token, const float *cand_score,
+                     const int32_t *cand_off, int max_cand, const int32_t *budget,
+                     const int32_t *ret_token, const int32_t *ret_parent, const int32_t *ret_off,
+                     const int32_t *table, int V, int k, float replace_thresh,
+                     const int32_t *ctx_len, const int32_t *row_off,
+                     int32_t *n_out, int32_t *parent, int32_t *token, int32_t *depth,
+                     int32_t *pos, uint64_t *mask, int8_t *src, int32_t *err_flag,
+                     graft_stream stream);
+
+/*
+ * Tree-masked grouped-query attention (Graft page, section 2, third step:
+ * one parallel verification of the flattened tree with its tree mask;
+ * TreeGraft page, section 3 and section 7 item 1: tree attention).
+ *
+ * For request b, node i < n[b], query head h (kv head h / (Hq/Hkv)):
+ *   out = softmax(scale * q . K^T) V  over cache slots 0 .. ctx_len[b]-1
+ *   and the tree slots ctx_len[b] + j with bit j of mask[row_off[b]+i].
+ * q, out  (device) bf16 [rows, Hq, d] with row = row_off[b] + i.
+ * kcache, vcache (device) bf16: slot s of kv head h of request b at
+ *   element kv_off[b] + h * kv_head_stride + s * d; tree node j's key and
+ *   value sit at slot ctx_len[b] + j.
+ * ctx_len, n (device int32 [B]); max_ctx, max_n (host) bound them (grid
+ *   sizing); a request above a bound is skipped with ERR_CAPACITY.
+ * lse (device fp32 [rows, Hq], natural log) may be NULL.
+ * d in {64, 128}; Hq % Hkv == 0; Hq / Hkv <= 16.
+ * ws (device) holds split-K partials: at least
+ *   graft_tree_attention_workspace_bytes(...) bytes (may be 0 -> ws NULL).
+ * Output is bf16 rounded to nearest even; softmax and accumulation fp32.
+ */
+size_t graft_tree_attention_workspace_bytes(int B, int Hq, int Hkv, int d, int max_ctx, int max_n);
+int graft_tree_attention(int B, int Hq, int Hkv, int d, float scale,
+                         const graft_bf16 *q, const graft_bf16 *kcache, const graft_bf16 *vcache,
+                         const int64_t *kv_off, int64_t kv_head_stride,
+                         const int32_t *ctx_len, int max_ctx, const int32_t *n, int max_n,
+                         const int32_t *row_off, const uint64_t *mask,
+                         graft_bf16 *out, float *lse, void *ws, size_t ws_bytes,
+                         int32_t *err_flag, graft_stream stream);
+
+/*
+ * lm-head and vocabulary top-k (Graft page, section 2: the verification
+ * pass yields each position's next-token distribution; the table keeps
+ * each token's top successors; greedy acceptance reads the argmax).
+ *
+ *   logits[m, v] = sum_h hidden[m, h] * W[v, h]     (fp32 accumulate)
+ *   topk_id[m, :] = the k ids of row m by (logit desc, id asc), topk_val
+ *   the matching logits; argmax = topk_id[m, 0].
+ * hidden (device bf16 [M, H]), w (device bf16 [V, H] row-major),
+ * logits (device fp32 [M, V]), topk_id (device int32 [M, k]),
+ * topk_val (device fp32 [M, k], may be NULL).
+ * Modes:  hidden && logits && k == 0      -> logits only
+ *         !hidden && logits && k > 0      -> top-k of the given logits
+ *         hidden && logits && k > 0       -> both, logits materialised
+ * H % 64 == 0; 1 <= k <= min(GRAFT_MAX_K, V).
+ * ws (device): graft_lmhead_topk_workspace_bytes(M, V, k) bytes.
+ */
+size_t graft_lmhead_topk_workspace_bytes(int M, int V, int k);
+int graft_lmhead_topk(int M, int H, int V, int k,
+                      const graft_bf16 *hidden, const graft_bf16 *w, float *logits,
+                      int32_t *topk_id, float *topk_val, void *ws, size_t ws_bytes,
+                      graft_stream stream);
+
+/*
+ * Greedy acceptance (Graft page, section 2, third step: draft and
+ * retrieved nodes face the same rule; TreeGraft page, sections 1 and 5:
+ * temperature 0, the accepted prefix stops at the first rejection).
+ * Node i > 0 is accepted iff token[i] == argmax[parent[i]] and its parent
+ * is accepted (argmax[r] = topk_id[r * k]); the root is accepted.
+ * Per request: best = the deepest accepted node (ties: lowest index),
+ *   acc_len[b] = depth(best) (draft tokens accepted, bonus excluded),
+ *   acc_path[b * 64 + t] = node index at depth t of best's root path for
+ *   t <= depth(best), -1 after it; bonus[b] = argmax[best].
+ * n, row_off, parent, token, topk_id: device, padded row layout.
+ * Outputs: device int32.  Malformed trees flag ERR_PARENT / ERR_CAPACITY
+ * and return acc_len 0, path [0], bonus argmax[0] (or -1 if n < 1).
+ */
+int graft_accept(int B, const int32_t *n, const int32_t *row_off,
+                 const int32_t *parent, const int32_t *token, const int32_t *topk_id, int k,
+                 int32_t *acc_len, int32_t *acc_path, int32_t *bonus, int32_t *err_flag,
+                 graft_stream stream);
+
+/*
+ * Host helper: the stage-adaptive retrieval template of R nodes (Graft
+ * page, section 2, second step: asymmetric, higher-ranked successors get
+ * more children and a deeper main chain; section 5: depth about 8 and
+ * width about 8 work best).  The pages give properties, not a node list;
+ * this builds the R best rank paths (r1..rd), d <= dmax, 0 <= r < k, by
+ * score prod 0.75/(r+1), ties to smaller depth then lexicographically
+ * smaller path.  Output in (host) tmpl_parent[R] (-1 = root) and
+ * tmpl_rank[R], topologically ordered.  dmax <= 8, k <= GRAFT_MAX_K,
+ * R <= GRAFT_MAX_NODES.
+ */
+int graft_make_template(int R, int k, int dmax, int32_t *tmpl_parent, int32_t *tmpl_rank);
+
+/*
+ * Host helper: Graft's stage budgets of 60 verify slots (Graft page,
+ * section 2, second step): pruning at checkpoint depth 0 keeps 8 draft
+ * nodes and retrieves 52; depth 1 keeps 24 and retrieves 36; depth 5 keeps
+ * 40 and retrieves 20; no pruning (stage -1) keeps the 60-node draft tree
+ * and retrieves none.  Draft counts include the root.
+ */
+int graft_stage_budget(int stage, int32_t *draft_nodes, int32_t *retrieved_nodes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRAFT_H */

@@ -1,0 +1,110 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+the header declares, validates host-checkable arguments without launching,
+and its host helpers agree with the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "graft.h")
+
+
+@pytest.fixture(scope="module")
+def native():
+    from draft_tree_verification_parent_amd import _native
+    if not os.path.exists(_native.LIB_PATH):
+        from draft_tree_verification_parent_amd import build
+        build.build()
+    return _native
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(graft_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_round(native):
+    names = declared_functions()
+    for n in ("graft_build_tree", "graft_tree_attention", "graft_lmhead_topk", "graft_accept",
+              "graft_table_update_retrieve"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(native):
+    lib = ctypes.CDLL(native.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+        assert n in native.SIGNATURES, f"{n} missing from the Python binding"
+
+
+def test_template_helper_matches_oracle(native):
+    from draft_tree_verification_parent_amd import api
+    from oracle.template import template
+    for R in range(0, 65, 3):
+        for k in (1, 2, 8, 10, 16):
+            for dmax in (1, 3, 8):
+                try:
+                    tp, tr, _ = template(R, k, dmax)
+                except ValueError:
+                    with pytest.raises(native.GraftError):
+                        api.graft_make_template(R, k, dmax)
+                    continue
+                gp, gr = api.graft_make_template(R, k, dmax)
+                assert gp.tolist() == tp and gr.tolist() == tr
+
+
+def test_stage_budgets(native):
+    from draft_tree_verification_parent_amd import api
+    # Graft page, section 2: 8/52, 24/36, 40/20 of 60 slots; no prune -> no retrieval
+    assert api.graft_stage_budget(0) == (8, 52)
+    assert api.graft_stage_budget(1) == (24, 36)
+    assert api.graft_stage_budget(5) == (40, 20)
+    assert api.graft_stage_budget(-1) == (60, 0)
+    with pytest.raises(native.GraftError):
+        api.graft_stage_budget(3)
+
+
+def test_host_argument_validation_launches_nothing(native):
+    L = native.lib()
+    E, U = native.GRAFT_EINVAL, native.GRAFT_EUNSUPPORTED
+    # lm-head / top-k
+    assert L.graft_lmhead_topk(4, 256, 100, 17, 1, 1, 1, 1, None, 1, 1 << 20, None) == E
+    assert L.graft_lmhead_topk(4, 100, 100, 4, 1, 1, 1, 1, None, 1, 1 << 20, None) == E
+    assert L.graft_lmhead_topk(4, 256, 100, 4, 1, 1, None, 1, None, 1, 1 << 20, None) == U
+    assert L.graft_lmhead_topk(4, 256, 100, 4, None, None, None, 1, None, 1, 1 << 20, None) == E
+    assert L.graft_lmhead_topk(4, 256, 100, 200, None, None, 1, 1, None, 1, 1 << 20, None) == E
+    assert L.graft_lmhead_topk(0, 256, 100, 4, None, None, 1, 1, None, None, 0, None) == 0
+    # attention
+    args = [1, 1, 1, 1, 1 << 20, 1, 100, 1, 10, 1, 1, 1, None, None, 0, None, None]
+    assert L.graft_tree_attention(1, 8, 2, 96, 0.1, *args) == U
+    assert L.graft_tree_attention(1, 8, 3, 128, 0.1, *args) == E
+    assert L.graft_tree_attention(0, 8, 2, 128, 0.1, *args) == 0
+    # build tree
+    bt = [1] * 24
+    assert L.graft_build_tree(1, 7, *bt[:4], 10, *bt[:5], 100, 8, 0.0, *bt[:11]) == E
+    assert L.graft_build_tree(1, 0, *bt[:4], 5000, *bt[:5], 100, 8, 0.0, *bt[:11]) == E
+    assert L.graft_build_tree(0, 0, *bt[:4], 10, *bt[:5], 100, 8, 0.0, *bt[:11]) == 0
+    # table
+    assert L.graft_table_update_retrieve(1, 100, 17, 0, None, None, 0, None, None, 0, None, None,
+                                         None, None, 0, None, None, None) == E
+    assert L.graft_table_update_retrieve(1, 100, 8, 1, 1, 1, 5000, 1, 1, 0, None, None, None,
+                                         None, 0, None, None, None) == E
+    assert L.graft_table_update_retrieve(1, 100, 8, 0, None, None, 0, None, None, 0, None, None,
+                                         None, None, 0, None, None, None) == 0
+    # accept
+    assert L.graft_accept(1, 1, 1, 1, 1, 1, 0, 1, 1, 1, None, None) == E
+    assert L.graft_accept(0, None, None, None, None, None, 8, None, None, None, None, None) == 0
+    assert b"k=" in L.graft_last_error()
+
+
+def test_workspace_sizes(native):
+    L = native.lib()
+    assert L.graft_lmhead_topk_workspace_bytes(60, 128256, 8) > 0
+    assert L.graft_lmhead_topk_workspace_bytes(0, 128256, 8) == 0
+    # tiny single-split attention needs no workspace; long context does
+    assert L.graft_tree_attention_workspace_bytes(1, 4, 2, 64, 100, 15) == 0
+    assert L.graft_tree_attention_workspace_bytes(1, 32, 8, 128, 32768, 63) > 0

@@ -1,0 +1,408 @@
+"""Per-kernel GPU parity and edge cases through the C ABI (bit-exact for
+integer work, 2e-2 + 1e-2 |ref| for floating point)."""
+import numpy as np
+import pytest
+
+from oracle import OracleError
+from oracle import accept as OAcc
+from oracle import attention as OA
+from oracle import lmhead as OL
+from oracle import table as OTab
+from oracle import topk as OT
+from oracle import tree as OTree
+from oracle.template import template as otemplate
+from synth import f32_to_bf16_bits
+from synth import workloads as W
+
+from _gpu_round import say, within_tol
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ERR_TOKEN, ERR_PARENT, ERR_NOT_CLOSED, ERR_CAPACITY, ERR_RANK = 1, 2, 4, 8, 16
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from draft_tree_verification_parent_amd import api as A
+    return A
+
+
+def dev_i32(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.int32)).cuda()
+
+
+def dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def err_buf():
+    return torch.zeros(1, dtype=torch.int32, device="cuda")
+
+
+# ----------------------------------------------------------------------------- top-k
+
+@pytest.mark.parametrize("M,V,k", [(1, 1000, 1), (3, 1001, 8), (5, 4096, 16), (60, 128256, 8),
+                                   (2, 17, 16), (7, 300000, 10)])
+def test_topk_matches_oracle(api, M, V, k):
+    say(f"[topk] M={M} V={V} k={k}")
+    r = np.random.default_rng(M * 7 + V)
+    x = r.integers(-20, 20, (M, V)).astype(np.float32)  # many ties
+    x[0, : min(V, 5)] = 0.0
+    x[0, min(V, 5) - 1] = -0.0
+    if M > 2:
+        x[2] = 3.0  # a constant row
+    logits = torch.from_numpy(x).cuda()
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    vals = torch.empty(M, k, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(api.graft_lmhead_topk_workspace_bytes(M, V, k), 1), dtype=torch.uint8, device="cuda")
+    api.graft_lmhead_topk(M, 0, V, k, None, None, logits, ids, vals, ws)
+    torch.cuda.synchronize()
+    eid, ev = OT.topk(x, k)
+    assert np.array_equal(ids.cpu().numpy(), eid)
+    assert np.array_equal(vals.cpu().numpy(), ev)
+
+
+# ----------------------------------------------------------------------------- lm-head
+
+@pytest.mark.parametrize("M,H,V", [(1, 64, 128), (15, 256, 1024), (65, 320, 1001), (130, 512, 777),
+                                   (60, 4096, 3000)])
+def test_lmhead_shapes(api, M, H, V):
+    say(f"[lmhead] M={M} H={H} V={V}")
+    r = np.random.default_rng(M + H + V)
+    h = f32_to_bf16_bits(r.standard_normal((M, H)).astype(np.float32))
+    w = f32_to_bf16_bits((0.02 * r.standard_normal((V, H))).astype(np.float32))
+    logits = torch.empty(M, V, dtype=torch.float32, device="cuda")
+    api.graft_lmhead_topk(M, H, V, 0, dev_bf16(h), dev_bf16(w), logits)
+    torch.cuda.synchronize()
+    ok, e = within_tol(logits.cpu().numpy().astype(np.float64), OL.logits(h, w).astype(np.float64))
+    assert ok, e
+
+
+def test_lmhead_exact_on_small_integers(api):
+    # integer-valued bf16 inputs: every product and partial sum is exact in
+    # fp32, so the GPU must equal the oracle bit for bit
+    r = np.random.default_rng(5)
+    M, H, V = 33, 448, 520
+    h = f32_to_bf16_bits(r.integers(-4, 5, (M, H)).astype(np.float32))
+    w = f32_to_bf16_bits(r.integers(-4, 5, (V, H)).astype(np.float32))
+    logits = torch.empty(M, V, dtype=torch.float32, device="cuda")
+    api.graft_lmhead_topk(M, H, V, 0, dev_bf16(h), dev_bf16(w), logits)
+    torch.cuda.synchronize()
+    assert np.array_equal(logits.cpu().numpy(), OL.logits(h, w))
+
+
+def test_lmhead_then_topk_in_one_call(api):
+    r = np.random.default_rng(9)
+    M, H, V, k = 20, 256, 5000, 10
+    h = f32_to_bf16_bits(r.standard_normal((M, H)).astype(np.float32))
+    w = f32_to_bf16_bits((0.02 * r.standard_normal((V, H))).astype(np.float32))
+    logits = torch.empty(M, V, dtype=torch.float32, device="cuda")
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(api.graft_lmhead_topk_workspace_bytes(M, V, k), 1), dtype=torch.uint8, device="cuda")
+    api.graft_lmhead_topk(M, H, V, k, dev_bf16(h), dev_bf16(w), logits, ids, None, ws)
+    torch.cuda.synchronize()
+    eid, _ = OT.topk(logits.cpu().numpy(), k)
+    assert np.array_equal(ids.cpu().numpy(), eid)
+
+
+# ----------------------------------------------------------------------------- accept
+
+def _accept_gpu(api, n, row_off, parent, token, argmax):
+    B = len(n)
+    k = 1
+    out_len = torch.empty(B, dtype=torch.int32, device="cuda")
+    out_path = torch.empty(B, 64, dtype=torch.int32, device="cuda")
+    out_bonus = torch.empty(B, dtype=torch.int32, device="cuda")
+    err = err_buf()
+    api.graft_accept(dev_i32(n), dev_i32(row_off), dev_i32(parent), dev_i32(token),
+                     dev_i32(np.asarray(argmax).reshape(-1, 1)), k, out_len, out_path, out_bonus, err)
+    torch.cuda.synchronize()
+    return out_len.cpu().numpy(), out_path.cpu().numpy(), out_bonus.cpu().numpy(), err.item()
+
+
+def test_accept_random_ragged_batch(api):
+    r = np.random.default_rng(3)
+    B = 200
+    n = r.integers(1, 65, B)
+    cap = n + r.integers(0, 4, B)
+    row_off = np.concatenate([[0], np.cumsum(cap)]).astype(np.int32)
+    rows = int(row_off[-1])
+    parent = np.full(rows, -7, np.int32)
+    token = r.integers(0, 3, rows).astype(np.int32)
+    argmax = r.integers(0, 3, rows).astype(np.int32)
+    for b in range(B):
+        o = row_off[b]
+        parent[o] = -1
+        for i in range(1, n[b]):
+            # bias towards chains so that deep accepted paths occur
+            parent[o + i] = i - 1 if r.random() < 0.6 else int(r.integers(0, i))
+    L, Pth, Bo, err = _accept_gpu(api, n, row_off, parent, token, argmax)
+    assert err == 0
+    lens, paths, bonus = OAcc.accept_batch(n, row_off, parent, token, argmax)
+    assert L.tolist() == lens and Bo.tolist() == bonus
+    for b in range(B):
+        assert Pth[b].tolist() == paths[b] + [-1] * (64 - len(paths[b]))
+    assert max(lens) >= 5
+
+
+def test_accept_full_chain_of_64(api):
+    n = np.array([64])
+    parent = np.arange(-1, 63, dtype=np.int32)
+    token = np.arange(64, dtype=np.int32)
+    argmax = np.arange(1, 65, dtype=np.int32)  # every edge matches
+    L, Pth, Bo, err = _accept_gpu(api, n, [0, 64], parent, token, argmax)
+    assert err == 0 and L[0] == 63 and Pth[0].tolist() == list(range(64)) and Bo[0] == 64
+
+
+def test_accept_malformed_tree_flags(api):
+    # a parent that does not precede its child: flagged, degenerate result
+    n = np.array([3, 2])
+    parent = np.array([-1, 2, 0, -1, 0], np.int32)
+    token = np.zeros(5, np.int32)
+    argmax = np.zeros(5, np.int32)
+    L, Pth, Bo, err = _accept_gpu(api, n, [0, 3, 5], parent, token, argmax)
+    assert err & ERR_PARENT
+    assert L[0] == 0 and Pth[0][0] == 0 and Pth[0][1] == -1
+    assert L[1] == 1  # the well-formed request is unaffected
+
+
+# ----------------------------------------------------------------------------- table
+
+def _table_gpu(api, table, n, row_off, token, topk, roots, tp, tr, toff):
+    t = dev_i32(table)
+    R = int(toff[-1])
+    ret = torch.full((max(R, 1),), -9, dtype=torch.int32, device="cuda")
+    err = err_buf()
+    api.graft_table_update_retrieve(t, dev_i32(n), dev_i32(row_off), int(row_off[-1]), dev_i32(token),
+                                    dev_i32(topk), dev_i32(roots), dev_i32(tp if R else [0]),
+                                    dev_i32(tr if R else [0]), dev_i32(toff), R, ret, err)
+    torch.cuda.synchronize()
+    return t.cpu().numpy(), ret.cpu().numpy()[:R], err.item()
+
+
+@pytest.mark.parametrize("rows", [1, 64, 960, 4096])
+def test_table_update_conflicts_and_retrieval(api, rows):
+    r = np.random.default_rng(rows)
+    V, k = 500, 8
+    table = np.stack([r.choice(V, k, replace=False) for _ in range(V)]).astype(np.int32)
+    B = max(1, rows // 60)
+    cuts = np.sort(r.choice(np.arange(1, rows), B - 1, replace=False)) if B > 1 else []
+    row_off = np.concatenate([[0], cuts, [rows]]).astype(np.int32)
+    cap = np.diff(row_off)
+    n = np.array([max(0, c - int(r.integers(0, 3))) for c in cap], np.int32)
+    token = r.integers(0, 40, rows).astype(np.int32)  # heavy same-token conflicts
+    topk = np.stack([r.choice(V, k, replace=False) for _ in range(rows)]).astype(np.int32)
+    # retrieval from roots that were just updated and from untouched ones
+    Bt = 5
+    roots = np.array([token[0], 3, 450, token[rows // 2], 499], np.int32)
+    tps, trs, toff = [], [], [0]
+    for b in range(Bt):
+        tp, tr, _ = otemplate([52, 36, 20, 0, 7][b], k, 8)
+        tps += tp
+        trs += tr
+        toff.append(toff[-1] + len(tp))
+    got_t, got_r, err = _table_gpu(api, table, n, row_off, token, topk, roots,
+                                   np.array(tps), np.array(trs), np.array(toff))
+    assert err == 0
+    exp_t = OTab.update(table, n, row_off, token, topk)
+    assert np.array_equal(got_t, exp_t)
+    exp_r = []
+    for b in range(Bt):
+        exp_r += OTab.retrieve(exp_t, int(roots[b]), tps[toff[b]:toff[b + 1]], trs[toff[b]:toff[b + 1]])
+    assert got_r.tolist() == exp_r
+
+
+def test_table_invalid_rows_are_flagged_and_skipped(api):
+    V, k = 50, 4
+    table = np.tile(np.arange(k, dtype=np.int32), (V, 1))
+    token = np.array([3, 77, 5], np.int32)  # 77 is outside the vocabulary
+    topk = np.array([[9, 8, 7, 6], [1, 2, 3, 4], [1, 2, 99, 4]], np.int32)  # row 2 has a bad id
+    got_t, _, err = _table_gpu(api, table, np.array([3]), np.array([0, 3]), token, topk,
+                               np.array([0]), np.zeros(0), np.zeros(0), np.array([0, 0]))
+    assert err & ERR_TOKEN
+    assert got_t[3].tolist() == [9, 8, 7, 6]
+    assert got_t[5].tolist() == [0, 1, 2, 3]  # skipped
+
+
+# ----------------------------------------------------------------------------- build tree
+
+def _build_gpu(api, mode, cands, budgets, rets, ctx, caps, table=None, V=1000, k=8, thresh=0.05):
+    B = len(cands)
+    cp = np.concatenate([c[0] for c in cands])
+    ct = np.concatenate([c[1] for c in cands])
+    cs = np.concatenate([c[2] for c in cands]).astype(np.float32)
+    coff = np.concatenate([[0], np.cumsum([len(c[0]) for c in cands])]).astype(np.int32)
+    row_off = np.concatenate([[0], np.cumsum(caps)]).astype(np.int32)
+    rows = int(row_off[-1])
+    rt = np.concatenate([x[0] for x in rets]) if rets else np.zeros(0, np.int32)
+    rp = np.concatenate([x[1] for x in rets]) if rets else np.zeros(0, np.int32)
+    roff = np.concatenate([[0], np.cumsum([len(x[0]) for x in rets])]).astype(np.int32) if rets else None
+    o = {key: torch.full((rows,), -5, dtype=torch.int32, device="cuda")
+         for key in ("parent", "token", "depth", "pos")}
+    mask = torch.zeros(rows, dtype=torch.int64, device="cuda")
+    src = torch.zeros(rows, dtype=torch.int8, device="cuda")
+    n_out = torch.empty(B, dtype=torch.int32, device="cuda")
+    err = err_buf()
+    tbl = dev_i32(table) if table is not None else None
+    api.graft_build_tree(mode, dev_i32(cp), dev_i32(ct), torch.from_numpy(cs).cuda(), dev_i32(coff),
+                         int(np.max(np.diff(coff))), dev_i32(budgets),
+                         dev_i32(rt if len(rt) else [0]) if rets else None,
+                         dev_i32(rp if len(rp) else [0]) if rets else None,
+                         dev_i32(roff) if rets else None, tbl, V, k, thresh, dev_i32(ctx),
+                         dev_i32(row_off), n_out, o["parent"], o["token"], o["depth"], o["pos"], mask, src, err)
+    torch.cuda.synchronize()
+    got = {key: v.cpu().numpy() for key, v in o.items()}
+    got["mask"] = mask.cpu().numpy().view(np.uint64)
+    got["src"] = src.cpu().numpy()
+    got["n"] = n_out.cpu().numpy()
+    return got, row_off, err.item()
+
+
+def test_build_ragged_batch_matches_oracle(api):
+    r = W.rng(77, "ragged")
+    V = 1000
+    cands, budgets, rets, caps, ctx = [], [], [], [], []
+    specs = [(8, 52), (24, 36), (40, 20), (60, 0), (63, 0), (1, 0), (5, 3), (64, 0)]
+    for j, (bud, R) in enumerate(specs):
+        cands.append(W.eagle_candidates(r, V, 5, 10, 10, int(r.integers(0, V))))
+        budgets.append(bud)
+        tp, tr, _ = otemplate(R, 8, 8)
+        rets.append((r.integers(0, V, R).astype(np.int32), np.array(tp, np.int32)))
+        caps.append(bud + R + j % 3)
+        ctx.append(int(r.integers(0, 70000)))
+    got, row_off, err = _build_gpu(api, 0, cands, budgets, rets, ctx, caps, V=V)
+    assert err == 0
+    exp = OTree.build_batch(np.concatenate([c[0] for c in cands]), np.concatenate([c[1] for c in cands]),
+                            np.concatenate([c[2] for c in cands]),
+                            np.concatenate([[0], np.cumsum([len(c[0]) for c in cands])]), budgets,
+                            np.concatenate([x[0] for x in rets]), np.concatenate([x[1] for x in rets]),
+                            np.concatenate([[0], np.cumsum([len(x[0]) for x in rets])]), ctx, V, row_off)
+    for key in ("n", "parent", "token", "depth", "pos", "mask", "src"):
+        assert np.array_equal(got[key], exp[key]), key
+
+
+def test_build_chain_of_64_and_capacity_overflow(api):
+    C = 64
+    chain = (np.arange(-1, C - 1, dtype=np.int32), np.arange(C, dtype=np.int32),
+             (0.99 ** np.arange(C)).astype(np.float32))
+    got, row_off, err = _build_gpu(api, 0, [chain, chain], [64, 64], None, [10, 0], [64, 63])
+    # request 0 fits; request 1 (64 nodes in 63 rows) is flagged and padded
+    assert err & ERR_CAPACITY
+    assert got["n"].tolist() == [64, 0]
+    assert got["mask"][63] == np.uint64(0xFFFFFFFFFFFFFFFF)
+    assert got["pos"][:64].tolist() == list(range(10, 74))
+    assert np.all(got["parent"][64:] == -1) and np.all(got["src"][64:] == -1)
+
+
+def test_build_not_closed_flag(api):
+    cand = (np.array([-1, 0, 1], np.int32), np.array([1, 2, 3], np.int32),
+            np.array([1.0, 0.1, 0.5], np.float32))
+    with pytest.raises(OracleError):
+        OTree.build_one(cand[0], cand[1], cand[2], 2, np.zeros(0), np.zeros(0), 0, 10)
+    got, _, err = _build_gpu(api, 0, [cand], [2], None, [0], [4])
+    assert err & ERR_NOT_CLOSED
+
+
+def test_build_static_replace_matches_oracle(api):
+    V, k = 151936, 8
+    tbl = W.zipf_table(W.rng(55, "t"), V, k)
+    cands, ctx = [], []
+    for b in range(16):
+        cands.append(W.eagle_candidates(W.rng(55, f"d{b}"), V, 5, 10, 10, b * 11))
+        ctx.append(4096 + b)
+    got, row_off, err = _build_gpu(api, 1, cands, [60] * 16, None, ctx, [60] * 16, table=tbl, V=V, k=k)
+    assert err == 0
+    exp = OTree.build_batch(np.concatenate([c[0] for c in cands]), np.concatenate([c[1] for c in cands]),
+                            np.concatenate([c[2] for c in cands]),
+                            np.concatenate([[0], np.cumsum([len(c[0]) for c in cands])]), [60] * 16,
+                            np.zeros(0), np.zeros(0), np.zeros(17, np.int32), ctx, V, row_off,
+                            static_replace=True, table=tbl, replace_thresh=0.05)
+    for key in ("n", "parent", "token", "depth", "pos", "mask", "src"):
+        assert np.array_equal(got[key], exp[key]), key
+    assert (got["src"] == 3).sum() > 100
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _attn_case(api, B, Hq, Hkv, d, ctxs, ns, seed, chain=False):
+    r = np.random.default_rng(seed)
+    cap = max(ctxs) + max(ns)
+    rows_cap = [n + 2 for n in ns]  # padded rows
+    row_off = np.concatenate([[0], np.cumsum(rows_cap)]).astype(np.int32)
+    rows = int(row_off[-1])
+    q = f32_to_bf16_bits(r.standard_normal((rows, Hq, d)).astype(np.float32))
+    kc = f32_to_bf16_bits(r.standard_normal((B, Hkv, cap, d)).astype(np.float32))
+    vc = f32_to_bf16_bits(r.standard_normal((B, Hkv, cap, d)).astype(np.float32))
+    mask = np.zeros(rows, np.uint64)
+    for b in range(B):
+        par = [-1] + [(i - 1 if chain else int(r.integers(0, i))) for i in range(1, ns[b])]
+        for i in range(ns[b]):
+            m = 0
+            for j in OTree.ancestors_or_self(par, i):
+                m |= 1 << j
+            mask[row_off[b] + i] = m
+    kv_off = (np.arange(B) * Hkv * cap * d).astype(np.int64)
+    scale = 1 / np.sqrt(d)
+    out = torch.zeros(rows, Hq, d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros(rows, Hq, dtype=torch.float32, device="cuda")
+    wsb = api.graft_tree_attention_workspace_bytes(B, Hq, Hkv, d, max(ctxs), max(ns))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    err = err_buf()
+    api.graft_tree_attention(Hq, Hkv, d, scale, dev_bf16(q), dev_bf16(kc.reshape(-1)), dev_bf16(vc.reshape(-1)),
+                             torch.from_numpy(kv_off).cuda(), cap * d, dev_i32(ctxs), max(ctxs), dev_i32(ns),
+                             max(ns), dev_i32(row_off), torch.from_numpy(mask.view(np.int64)).cuda(), out, lse,
+                             ws, err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    got = out.float().cpu().numpy()
+    got_lse = lse.cpu().numpy()
+    qf = OL.bf16_to_f64(q).reshape(q.shape)
+    Ks = [OL.bf16_to_f64(kc[b]).reshape(Hkv, cap, d) for b in range(B)]
+    Vs = [OL.bf16_to_f64(vc[b]).reshape(Hkv, cap, d) for b in range(B)]
+    ref = OA.tree_attention(qf, Ks, Vs, ctxs, ns, row_off, mask, scale)
+    worst = 0.0
+    for (b, i), (o, l) in ref.items():
+        rr = int(row_off[b]) + i
+        ok, e = within_tol(got[rr].astype(np.float64), o)
+        assert ok, (b, i, e)
+        worst = max(worst, e)
+        assert np.all(np.abs(got_lse[rr] - l) <= 1e-3 + 1e-4 * np.abs(l))
+    return worst
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,ctxs,ns", [
+    (1, 4, 2, 64, [256], [15]),          # tiny config shape
+    (1, 4, 2, 64, [0], [7]),             # no context at all
+    (3, 32, 8, 128, [100, 3000, 37], [60, 1, 33]),   # ragged batch, single-node tree
+    (2, 40, 8, 128, [5000, 1234], [60, 60]),         # G = 5, 300 rows (two row groups)
+    (1, 8, 1, 128, [20000], [64]),                   # G = 8, many splits
+    (2, 16, 16, 64, [511, 513], [64, 2]),            # G = 1
+])
+def test_attention_cases(api, B, Hq, Hkv, d, ctxs, ns):
+    say(f"[attention] B={B} Hq={Hq} Hkv={Hkv} d={d} ctx={ctxs} n={ns}")
+    worst = _attn_case(api, B, Hq, Hkv, d, ctxs, ns, seed=B * 100 + Hq)
+    say(f"[attention] max abs err {worst:.3g}")
+
+
+def test_attention_chain_tree(api):
+    _attn_case(api, 1, 8, 2, 128, [777], [64], seed=5, chain=True)
+
+
+def test_attention_length_above_bound_is_flagged(api):
+    # ctx_len above max_ctx: the request is skipped and flagged, no fault
+    B, Hq, Hkv, d = 1, 4, 2, 64
+    cap = 300
+    q = torch.zeros(4, Hq, d, dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros(Hkv * cap * d, dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros(4, Hq, d, dtype=torch.bfloat16, device="cuda")
+    err = err_buf()
+    ws = torch.empty(max(api.graft_tree_attention_workspace_bytes(B, Hq, Hkv, d, 100, 4), 1),
+                     dtype=torch.uint8, device="cuda")
+    api.graft_tree_attention(Hq, Hkv, d, 0.125, q, kc, kc, torch.zeros(1, dtype=torch.int64, device="cuda"),
+                             cap * d, dev_i32([250]), 100, dev_i32([4]), 4, dev_i32([0, 4]),
+                             torch.full((4,), 1, dtype=torch.int64, device="cuda"), out, None, ws, err)
+    torch.cuda.synchronize()
+    assert err.item() & ERR_CAPACITY

@@ -1,0 +1,136 @@
+"""Full-round parity on the GPU for the five workloads, stage by stage on
+identical inputs, through the C ABI.
+
+Integer outputs (table, retrieved tokens, tree arrays, top-k ids, accepted
+path) must be bit-exact.  Attention and logits must be within
+|gpu - ref| <= 2e-2 + 1e-2 |ref| of the fp64 oracle.  Top-k and acceptance
+run in the oracle on the GPU's own fp32 logits (ranking decisions taken in
+the same precision on both sides)."""
+import numpy as np
+import pytest
+
+from oracle import accept as OAcc
+from oracle import attention as OA
+from oracle import lmhead as OL
+from oracle import round as OR
+from oracle import topk as OT
+
+from _gpu_round import bf16_tensor_to_f64, run_gpu_round, say, within_tol
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _sample_nodes(rng, n, per_request):
+    nodes = []
+    for b, nb in enumerate(n):
+        nb = int(nb)
+        pick = range(nb) if per_request >= nb else sorted(rng.choice(nb, per_request, replace=False))
+        nodes += [(b, int(i)) for i in pick]
+    return nodes
+
+
+ATTN_SAMPLES = {1: 99, 2: 99, 3: 12, 4: 6, 5: 2}
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_round_parity(cfg):
+    _need_gpu()
+    wl, ri, w, ts, hidden, vr = run_gpu_round(cfg)
+    rng = np.random.default_rng(1000 + cfg)
+    assert vr.err.item() == 0
+
+    # table update (previous round's nodes) and retrieval
+    assert np.array_equal(vr.table.cpu().numpy(), ts["table"])
+    if vr.tmpl_rows:
+        assert np.array_equal(vr.ret_token[: vr.tmpl_rows].cpu().numpy(), ts["ret_token"])
+
+    # tree build: bit-exact, padded layout included
+    tree = ts["tree"]
+    g = vr.tree_host()
+    for key in ("n", "parent", "token", "depth", "pos", "mask", "src"):
+        assert np.array_equal(g[key], tree[key]), key
+
+    # tree attention on sampled nodes
+    nodes = _sample_nodes(rng, tree["n"], ATTN_SAMPLES[cfg])
+    q = OL.bf16_to_f64(ri.q).reshape(ri.q.shape)
+    Ks, Vs = {}, {}
+    for b in sorted({b for b, _ in nodes}):
+        Ks[b], Vs[b] = OR.kv_f64(ri, b)
+    out = bf16_tensor_to_f64(vr.attn_out)
+    lse = vr.lse.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for b in sorted(Ks):
+        sub = [(bb, i) for bb, i in nodes if bb == b]
+        KL = [None] * ri.B
+        VL = [None] * ri.B
+        KL[b], VL[b] = Ks[b], Vs[b]
+        ref = OA.tree_attention(q, KL, VL, ri.ctx_len, tree["n"], ri.row_off, tree["mask"], ri.scale,
+                                nodes=sub)
+        for (bb, i), (o, l) in ref.items():
+            r = int(ri.row_off[bb]) + i
+            ok, e = within_tol(out[r], o)
+            assert ok, f"attention row {(bb, i)} max err {e}"
+            worst = max(worst, e)
+            assert np.all(np.abs(lse[r] - l) <= 1e-3 + 1e-4 * np.abs(l))
+    say(f"[attention] cfg {cfg}: {len(nodes)} nodes, max abs err {worst:.3g}")
+
+    # lm-head on sampled vocabulary columns (plus each row's GPU top-k ids)
+    logits = vr.logits.cpu().numpy()
+    topk_id = vr.topk_id.cpu().numpy()
+    topk_val = vr.topk_val.cpu().numpy()
+    cols = np.unique(np.concatenate([rng.choice(ri.V, min(512, ri.V), replace=False), topk_id.ravel()]))
+    ref = OL.logits(hidden, w[cols])
+    ok, e = within_tol(logits[:, cols].astype(np.float64), ref.astype(np.float64))
+    assert ok, f"logits max err {e}"
+    say(f"[lm-head] cfg {cfg}: {logits.shape[0]} rows x {len(cols)} cols, max abs err {e:.3g}")
+
+    # top-k: exact on sampled rows; argmax property on every row
+    rows = np.arange(logits.shape[0]) if logits.shape[0] <= 64 else np.sort(
+        rng.choice(logits.shape[0], 96, replace=False))
+    ids, vals = OT.topk(logits[rows], ri.k)
+    assert np.array_equal(topk_id[rows], ids)
+    assert np.array_equal(topk_val[rows], vals)
+    assert np.array_equal(topk_id[:, 0], np.argmax(logits, axis=1))
+
+    # acceptance on the GPU's tree and argmax
+    lens, paths, bonus = OAcc.accept_batch(g["n"], ri.row_off, g["parent"], g["token"], topk_id[:, 0])
+    acc_len = vr.acc_len.cpu().numpy()
+    acc_path = vr.acc_path.cpu().numpy()
+    assert acc_len.tolist() == lens
+    assert vr.bonus.cpu().numpy().tolist() == bonus
+    for b in range(ri.B):
+        expect = paths[b] + [-1] * (64 - len(paths[b]))
+        assert acc_path[b].tolist() == expect
+    say(f"[accept] cfg {cfg}: accepted lengths {lens[:8]}")
+
+
+def test_end_to_end_argmax_where_margin_is_clear():
+    """Rows whose fp64 top-1/top-2 logit margin is far above the lm-head's
+    error take the same argmax on the GPU as in the oracle (cfg 2)."""
+    _need_gpu()
+    wl, ri, w, ts, hidden, vr = run_gpu_round(2)
+    gpu_arg = vr.topk_id.cpu().numpy()[:, 0]
+    rows = np.arange(8)
+    best = np.full(len(rows), -np.inf)
+    second = np.full(len(rows), -np.inf)
+    arg = np.zeros(len(rows), np.int64)
+    for c0 in range(0, ri.V, 16384):
+        lg = OL.logits(hidden[rows], w[c0:c0 + 16384]).astype(np.float64)
+        for j in range(len(rows)):
+            o = np.argsort(-lg[j], kind="stable")[:2]
+            for idx in o:
+                v = lg[j, idx]
+                if v > best[j]:
+                    second[j], best[j], arg[j] = best[j], v, c0 + idx
+                elif v > second[j]:
+                    second[j] = v
+    clear = (best - second) > 1e-3
+    assert clear.sum() >= 4
+    assert np.array_equal(gpu_arg[rows][clear], arg[clear])
+    say(f"[e2e] {int(clear.sum())} of {len(rows)} rows have a clear margin; all match")
