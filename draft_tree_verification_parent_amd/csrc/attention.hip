@@ -166,9 +166,12 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(Params P) {
     __syncthreads();
     if (stager) {
       *reinterpret_cast<u32x4 *>(&sm.k[st_key * Smem<D>::KSTR + st_col * 8]) = kreg;
-      const bf16x8 vv = __builtin_bit_cast(bf16x8, vreg);
+      // element e of the 16-byte piece is bits [16(e&1), 16(e&1)+16) of word e/2
+      // (extracting lanes of a __bf16 vector here miscompiled: every lane read as lane 0)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm.vt[(st_col * 8 + e) * Smem<D>::VSTR + st_key] = __builtin_bit_cast(graft_bf16, vv[e]);
+      for (int e = 0; e < 8; ++e)
+        sm.vt[(st_col * 8 + e) * Smem<D>::VSTR + st_key] =
+            static_cast<graft_bf16>((vreg[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
     }
     __syncthreads();
     if (c0 + KCH < k_end) fetch(c0 + KCH);
