@@ -115,7 +115,7 @@ def main():
         print(json.dumps({"copy_probe_bytes": n * 4, "launches": 5}))
         return
 
-    from draft_tree_verification_parent_amd.verify_round import STEPS, VerifyRound
+    from draft_tree_verification_parent_amd.verify_round import VerifyRound
     from synth import workloads as W
 
     wl = W.WORKLOADS[args.cfg]
@@ -175,24 +175,24 @@ def main():
     value = tokens * args.steps / (total_ms / 1e3)
 
     M, H, V = vr.rows, wl.H, wl.V
-    lm_bytes = V * H * 2 + M * H * 2 + M * V * 4       # W once, hidden once, logits written once
+    # fused lm-head + top-k: W once, hidden once, k (id, value) pairs per row out
+    lm_bytes = V * H * 2 + M * H * 2 + M * ri.k * 8
     lm_flops = 2.0 * M * H * V
-    lm_s = step_us["lmhead"] * 1e-6
+    lm_s = step_us["lmhead_topk"] * 1e-6
     achieved = lm_bytes / lm_s / 1e9
     wkey = f"cfg{args.cfg}"
     traffic = measured_traffic(wkey)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "lmhead_kernel", "algorithmic_bytes_per_launch": lm_bytes,
+                "kernel": (f"lmhead_kernel<{128 if H % 128 == 0 else 64},true,{8 if ri.k <= 8 else 16}> + "
+                           f"topk_merge_kernel<{8 if ri.k <= 8 else 16}> (one graft_lmhead_topk call)"),
+                "algorithmic_bytes_per_launch": lm_bytes,
                 "mfma_frac": round(lm_flops / lm_s / 1e12 / MFMA_BF16_PEAK_TFS, 4)}
     # secondary kernels, same convention (algorithmic bytes / measured time)
-    tk_bytes = M * V * 4
     att_keys = int(np.sum(ri.ctx_len)) + tokens
     att_bytes = 2 * att_keys * wl.Hkv * wl.d * 2 + 2 * tokens * wl.Hq * wl.d * 2
     att_flops = 4.0 * tokens * wl.Hq * wl.d * (float(np.mean(ri.ctx_len)) + ri.N)
     kernels = {
-        "topk": {"us": round(step_us["topk"], 2),
-                 "hbm_frac": round(tk_bytes / (step_us["topk"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "tree_attention": {"us": round(step_us["tree_attention"], 2),
                            "hbm_frac": round(att_bytes / (step_us["tree_attention"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                            "mfma_frac": round(att_flops / (step_us["tree_attention"] * 1e-6) / 1e12

@@ -36,7 +36,7 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int KCH = 32;      // keys per staged chunk (two 16-key MFMA blocks)
+constexpr int KCH = 64;      // keys per staged chunk (four 16-key MFMA blocks)
 constexpr int MIN_SPLIT = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -44,12 +44,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ inline bf16x8 zero8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
 __device__ inline u32x4 load16(const graft_bf16 *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
+// Double-buffered K and V^T tiles of one KCH-key chunk.
 template <int D>
 struct Smem {
   static constexpr int KSTR = D + 8;    // bf16 per K row (16 B pad)
-  static constexpr int VSTR = KCH + 4;  // bf16 per V^T row (8 B pad)
-  graft_bf16 k[KCH * KSTR];
-  graft_bf16 vt[D * VSTR];
+  static constexpr int VSTR = KCH + 4;  // bf16 per V^T row (8 B pad: 16 rows of a fragment hit 32 banks)
+  graft_bf16 k[2][KCH * KSTR];
+  graft_bf16 vt[2][D * VSTR];
 };
 
 struct Params {
@@ -75,7 +76,7 @@ struct Params {
 };
 
 // Returns false (and flags once) when the request's lengths exceed the
-// bounds the grid was sized for.
+// bounds the grid was sized for or its row capacity.
 __device__ inline bool request_ok(const Params &P, int b, int &ctx, int &n) {
   ctx = P.ctx_len[b];
   n = P.n[b];
@@ -85,11 +86,21 @@ __device__ inline bool request_ok(const Params &P, int b, int &ctx, int &n) {
   return ok;
 }
 
+// Registers of one chunk in flight: KP 16-byte K pieces and (for threads that
+// stage V) the same 8 head-dim columns of two consecutive keys.
+template <int D>
+struct Stage {
+  static constexpr int KP = KCH * D / 8 / kThreads;  // K pieces per thread
+  u32x4 k[KP];
+  u32x4 va, vb;
+};
+
 template <int D, int RBW>
-__global__ __launch_bounds__(kThreads) void tree_attn_kernel(Params P) {
+__global__ __launch_bounds__(kThreads, RBW == 1 ? 2 : 1) void tree_attn_kernel(Params P) {
   constexpr int DS = D / 32;  // MFMA k-steps over the head dim
   constexpr int DB = D / 16;  // 16-wide output blocks over the head dim
-  constexpr int PIECES = KCH * D / 8;
+  constexpr int KP = Stage<D>::KP;
+  constexpr int VTHREADS = (KCH / 2) * (D / 8);  // threads staging a V key pair
   __shared__ __attribute__((aligned(16))) Smem<D> sm;
 
   const int b = blockIdx.z;
@@ -105,6 +116,7 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(Params P) {
   const int rows_total = n * P.G;
   const int row_lo = rg * P.rows_per_wg;
   if (row_lo >= rows_total) return;
+  const int nch = (k_end - k_begin + KCH - 1) / KCH;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -121,16 +133,17 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(Params P) {
 #pragma unroll
   for (int j = 0; j < RBW; ++j) {
     const int rb0 = row_lo + (wave * RBW + j) * 16;
-    active[j] = rb0 < rows_total;
+    // wave-uniform; readfirstlane lets the compiler branch on a scalar
+    // instead of masking every MFMA below
+    active[j] = __builtin_amdgcn_readfirstlane(rb0 < rows_total ? 1 : 0) != 0;
     const int r = rb0 + l16;
     rvalid[j] = r < rows_total;
-    const int node = r / P.G;
-    const int hq = h * P.G + (r - node * P.G);
+    const int node = (rvalid[j] ? r : 0) / P.G;
+    const int hq = h * P.G + ((rvalid[j] ? r : 0) - node * P.G);
     mrow[j] = rvalid[j] ? P.mask[r_off + node] : 0ull;
     const graft_bf16 *qp = P.q + (static_cast<size_t>(r_off + node) * P.Hq + hq) * D + 8 * g;
 #pragma unroll
-    for (int s = 0; s < DS; ++s)
-      qf[j][s] = rvalid[j] ? __builtin_bit_cast(bf16x8, load16(qp + s * 32)) : zero8();
+    for (int s = 0; s < DS; ++s) qf[j][s] = rvalid[j] ? __builtin_bit_cast(bf16x8, load16(qp + s * 32)) : zero8();
   }
 
   f32x4 oacc[RBW][DB];
@@ -143,109 +156,172 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(Params P) {
     for (int db = 0; db < DB; ++db) oacc[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- staging: each thread moves one 16-byte piece of K and of V per chunk
-  const bool stager = tid < PIECES;
-  const int st_key = tid / (D / 8);
-  const int st_col = tid - st_key * (D / 8);
+  // ---- staging.  Loads are unconditional: slots past k_end read the last
+  // valid slot (their scores are masked and their P is 0), which keeps the
+  // compiler from draining the memory pipeline at branch joins.
   const size_t kv_base = static_cast<size_t>(P.kv_off[b]) + static_cast<size_t>(h) * P.head_stride;
-  u32x4 kreg = u32x4{0u, 0u, 0u, 0u}, vreg = u32x4{0u, 0u, 0u, 0u};
-  auto fetch = [&](int c0) {
-    const int slot = c0 + st_key;
-    if (stager && slot < k_end) {
-      const size_t off = kv_base + static_cast<size_t>(slot) * D + st_col * 8;
-      kreg = load16(P.kc + off);
-      vreg = load16(P.vc + off);
-    } else {
-      kreg = u32x4{0u, 0u, 0u, 0u};
-      vreg = u32x4{0u, 0u, 0u, 0u};
+  // every thread stages V at d = 128; at d = 64 waves 0-3 do (wave-uniform)
+  const bool vstager = VTHREADS >= kThreads || __builtin_amdgcn_readfirstlane(tid < VTHREADS ? 1 : 0) != 0;
+  const int vcol = tid % (D / 8);
+  const int vkp = tid / (D / 8);  // key pair
+  auto fetch = [&](Stage<D> &st, int c) {
+    const int c0 = k_begin + c * KCH;
+#pragma unroll
+    for (int j = 0; j < KP; ++j) {
+      const int p = tid + j * kThreads;
+      const int key = p / (D / 8);
+      const int col = p - key * (D / 8);
+      const int slot = min(c0 + key, k_end - 1);
+      st.k[j] = load16(P.kc + kv_base + static_cast<size_t>(slot) * D + col * 8);
+    }
+    if (vstager) {
+      const int s0 = min(c0 + 2 * vkp, k_end - 1);
+      const int s1 = min(c0 + 2 * vkp + 1, k_end - 1);
+      st.va = load16(P.vc + kv_base + static_cast<size_t>(s0) * D + vcol * 8);
+      st.vb = load16(P.vc + kv_base + static_cast<size_t>(s1) * D + vcol * 8);
     }
   };
-  fetch(k_begin);
-
-  for (int c0 = k_begin; c0 < k_end; c0 += KCH) {
-    __syncthreads();
-    if (stager) {
-      *reinterpret_cast<u32x4 *>(&sm.k[st_key * Smem<D>::KSTR + st_col * 8]) = kreg;
-      // element e of the 16-byte piece is bits [16(e&1), 16(e&1)+16) of word e/2
-      // (extracting lanes of a __bf16 vector here miscompiled: every lane read as lane 0)
+  auto store = [&](const Stage<D> &st, int buf) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sm.vt[(st_col * 8 + e) * Smem<D>::VSTR + st_key] =
-            static_cast<graft_bf16>((vreg[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu);
+    for (int j = 0; j < KP; ++j) {
+      const int p = tid + j * kThreads;
+      const int key = p / (D / 8);
+      const int col = p - key * (D / 8);
+      *reinterpret_cast<u32x4 *>(&sm.k[buf][key * Smem<D>::KSTR + col * 8]) = st.k[j];
     }
-    __syncthreads();
-    if (c0 + KCH < k_end) fetch(c0 + KCH);
-
-    // S^T blocks: sacc[j][kb][i] = S[row l16][key c0 + kb*16 + 4g + i]
-    f32x4 sacc[RBW][2];
+    if (vstager) {
+      // V^T[d][2kp], V^T[d][2kp+1] packed into one 32-bit word per head dim
 #pragma unroll
-    for (int j = 0; j < RBW; ++j) {
-      sacc[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      sacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&sm.k[(kb * 16 + l16) * Smem<D>::KSTR + s * 32 + 8 * g]);
-#pragma unroll
-        for (int j = 0; j < RBW; ++j)
-          if (active[j]) sacc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j][s], sacc[j][kb], 0, 0, 0);
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t a = st.va[e >> 1], bw = st.vb[e >> 1];
+        const uint32_t word = (e & 1) ? ((a >> 16) | (bw & 0xFFFF0000u)) : ((a & 0xFFFFu) | (bw << 16));
+        *reinterpret_cast<uint32_t *>(&sm.vt[buf][(vcol * 8 + e) * Smem<D>::VSTR + 2 * vkp]) = word;
       }
     }
-
-    // online softmax (base 2) and P^T operands
-    bf16x8 pb[RBW];
+  };
+  // One chunk = two 32-key halves; each half runs S^T, the online-softmax
+  // update and O^T += V^T . P^T, so only two S^T blocks are live at a time.
+  auto compute = [&](int c, int buf) {
 #pragma unroll
-    for (int j = 0; j < RBW; ++j) {
-      if (!active[j]) continue;
-      float x[8];
-      float cmax = -INFINITY;
+    for (int t = 0; t < 2; ++t) {
+      const int c0 = k_begin + c * KCH + 32 * t;
+      // S^T blocks: sacc[j][kb][i] = S[row l16][key c0 + kb*16 + 4g + i]
+      f32x4 sacc[RBW][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int j = 0; j < RBW; ++j) {
+        sacc[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = c0 + kb * 16 + 4 * g + i;
-          bool vis = key < k_end;
-          if (vis && key >= ctx) vis = (mrow[j] >> (key - ctx)) & 1ull;
-          const float v = vis ? sacc[j][kb][i] * P.scale_log2 : -INFINITY;
-          x[kb * 4 + i] = v;
-          cmax = fmaxf(cmax, v);
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+              &sm.k[buf][(32 * t + kb * 16 + l16) * Smem<D>::KSTR + s * 32 + 8 * g]);
+#pragma unroll
+          for (int j = 0; j < RBW; ++j)
+            if (active[j]) sacc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j][s], sacc[j][kb], 0, 0, 0);
         }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-      const float m_new = fmaxf(m_run[j], cmax);
-      float alpha = 1.f;
-      float psum = 0.f;
-      if (m_new != -INFINITY) {
-        alpha = exp2f(m_run[j] - m_new);
+      }
+      // online softmax (base 2) and the P^T operand of this half.  A half
+      // that lies entirely inside the context needs no mask (uniform test).
+      const bool unmasked = c0 + 32 <= ctx && c0 + 32 <= k_end;
+      bf16x8 pb[RBW];
+#pragma unroll
+      for (int j = 0; j < RBW; ++j) {
+        if (!active[j]) continue;
+        // raw scores; the scale is folded into the exp2 argument below
+        float x[8];
+        if (unmasked) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[kb * 4 + i] = sacc[j][kb][i];
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = c0 + kb * 16 + 4 * g + i;
+              const bool tree_vis = ((mrow[j] >> ((key - ctx) & 63)) & 1ull) != 0;
+              const bool vis = (key < k_end) & ((key < ctx) | tree_vis);  // no short-circuit branches
+              x[kb * 4 + i] = vis ? sacc[j][kb][i] : -INFINITY;
+            }
+        }
+        float cmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+        cmax *= P.scale_log2;  // scale > 0: max commutes with it
+        // Lazy rescaling: the running max m only moves when some row of the
+        // wave sees a score more than 8 (log2 units) above it, so p stays
+        // <= 2^8 and O, l keep sharing the same m (the final O / l is
+        // unchanged); most halves then skip the O rescale entirely.
+        const bool grow = cmax > m_run[j] + 8.f;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
+          // rows that do not grow keep alpha = 1 (also when m is still -inf)
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[j] - cmax) : 1.f;  // 0 from -inf
+          l_run[j] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[j][db] *= alpha;
+          m_run[j] = grow ? cmax : m_run[j];
+        }
+        // rows with nothing visible yet keep m = -inf: shift by 0 (p = 0)
+        const float m_use = m_run[j] == -INFINITY ? 0.f : m_run[j];
+        float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          x[e] = exp2f(x[e] - m_new);
+          x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], P.scale_log2, -m_use));
           psum += x[e];
         }
-      } else {
+        l_run[j] += psum;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        for (int e = 0; e < 8; ++e) pb[j][e] = static_cast<__bf16>(x[e]);
       }
-      m_run[j] = m_new;
-      l_run[j] = l_run[j] * alpha + psum;
+      // O^T += V^T . P^T (keys {4g..4g+3} and {16+4g..16+4g+3} of the half)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[j][db] *= alpha;
+      for (int db = 0; db < DB; ++db) {
+        const graft_bf16 *vrow = &sm.vt[buf][(db * 16 + l16) * Smem<D>::VSTR + 32 * t];
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + 4 * g);
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 16 + 4 * g);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[j][e] = static_cast<__bf16>(x[e]);
+        for (int j = 0; j < RBW; ++j)
+          if (active[j]) oacc[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[j], oacc[j][db], 0, 0, 0);
+      }
     }
+  };
 
-    // O^T += V^T . P^T
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const graft_bf16 *vrow = &sm.vt[(db * 16 + l16) * Smem<D>::VSTR];
-      const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + 4 * g);
-      const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 16 + 4 * g);
-      const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-      for (int j = 0; j < RBW; ++j)
-        if (active[j]) oacc[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[j], oacc[j][db], 0, 0, 0);
+  if constexpr (RBW < 3) {
+    // Two register stages in strict ping-pong and two LDS buffers: while
+    // chunk c is computed, chunks c+1 and c+2 are in flight.
+    Stage<D> A, Bst;
+    fetch(A, 0);
+    store(A, 0);
+    fetch(A, min(1, nch - 1));
+    __syncthreads();
+    for (int c = 0; c < nch; c += 2) {
+      fetch(Bst, min(c + 2, nch - 1));
+      compute(c, 0);
+      store(A, 1);
+      __syncthreads();
+      if (c + 1 >= nch) break;
+      fetch(A, min(c + 3, nch - 1));
+      compute(c + 1, 1);
+      store(Bst, 0);
+      __syncthreads();
+    }
+  } else {
+    // three row blocks per wave leave registers for one stage only: chunk c+1
+    // is in flight while chunk c is computed
+    Stage<D> A;
+    fetch(A, 0);
+    store(A, 0);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      fetch(A, min(c + 1, nch - 1));
+      compute(c, c & 1);
+      store(A, (c + 1) & 1);
+      __syncthreads();
     }
   }
 
@@ -284,11 +360,13 @@ __global__ __launch_bounds__(kThreads) void tree_attn_kernel(Params P) {
   }
 }
 
-// One thread per 4 output columns of one (request, KV head, query row).
+// Combines the splits of one (request, KV head, query row): D/4 lanes per
+// row, each owning 4 head-dim columns; one pass with a running maximum, the
+// split loads unrolled so their latencies overlap.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(Params P) {
-  constexpr int TPR = D / 4;         // threads per row
-  constexpr int RPB = 256 / TPR;     // rows per block
+  constexpr int TPR = D / 4;      // threads per row
+  constexpr int RPB = 256 / TPR;  // rows per block
   const int b = blockIdx.z;
   const int h = blockIdx.y;
   const int r = blockIdx.x * RPB + threadIdx.x / TPR;
@@ -299,17 +377,29 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(Params P) {
   const int L = ctx + n;
   const int ns = (L + P.split_len - 1) / P.split_len;
   const size_t base = (static_cast<size_t>(b) * P.Hkv + h) * P.nsplit * P.rows_cap + r;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, P.ws_ml[(base + static_cast<size_t>(s) * P.rows_cap) * 2]);
-  float wsum = 0.f;
+  float M = -INFINITY, wsum = 0.f;
   f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < ns; ++s) {
-    const size_t slot = base + static_cast<size_t>(s) * P.rows_cap;
-    const float ms = P.ws_ml[slot * 2];
-    if (ms == -INFINITY) continue;
-    const float wgt = exp2f(ms - M);
-    wsum += wgt * P.ws_ml[slot * 2 + 1];
-    o += wgt * *reinterpret_cast<const f32x4 *>(P.ws_o + slot * D + c);
+  constexpr int U = 4;
+  for (int s0 = 0; s0 < ns; s0 += U) {
+    float ms[U], ls[U];
+    f32x4 os[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t slot = base + static_cast<size_t>(min(s0 + u, ns - 1)) * P.rows_cap;
+      ms[u] = P.ws_ml[slot * 2];
+      ls[u] = P.ws_ml[slot * 2 + 1];
+      os[u] = *reinterpret_cast<const f32x4 *>(P.ws_o + slot * D + c);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u >= ns || ms[u] == -INFINITY) continue;
+      const float Mn = fmaxf(M, ms[u]);
+      const float a = exp2f(M - Mn);   // 0 when M was -inf
+      const float w = exp2f(ms[u] - Mn);
+      wsum = wsum * a + w * ls[u];
+      o = o * a + os[u] * w;
+      M = Mn;
+    }
   }
   const int node = r / P.G;
   const int hq = h * P.G + (r - node * P.G);
@@ -332,16 +422,21 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int max_n) {
   const int G = Hq / Hkv;
   const int rows = max_n * G;
   const int rb = (rows + 15) / 16;
-  // at most 3 row blocks per wave: 4 spills registers at d = 128
+  const long long L = static_cast<long long>(max_ctx) + max_n;
+  const long long min_splits = (L + MIN_SPLIT - 1) / MIN_SPLIT;
+  // fewest row groups that fit (at most 3 row blocks per wave: 4 spill at
+  // d = 128), unless even the finest key split leaves the chip half idle --
+  // then one row block per wave (two resident workgroups per CU, more groups)
   if (rb <= kWaves) p.rbw = 1;
   else if (rb <= 2 * kWaves) p.rbw = 2;
   else p.rbw = 3;
+  if (p.rbw > 1 && static_cast<long long>(B) * Hkv * ((rb + kWaves * p.rbw - 1) / (kWaves * p.rbw)) * min_splits < 256)
+    p.rbw = 1;
   p.rows_per_wg = kWaves * p.rbw * 16;
   p.row_groups = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
   p.rows_cap = rb * 16;
-  const long long L = static_cast<long long>(max_ctx) + max_n;
   const long long units = static_cast<long long>(B) * Hkv * p.row_groups;
-  long long want = units > 0 ? (512 + units - 1) / units : 1;
+  long long want = units > 0 ? (384 + units - 1) / units : 1;
   if (want < 1) want = 1;
   long long len = (L + want - 1) / want;
   len = (len + KCH - 1) / KCH * KCH;

@@ -10,7 +10,8 @@
 // (Graft page, section 4, batched-serving paragraph).
 //
 // One workgroup per request.  Ranking is a rank count in LDS (candidate
-// pools are a few hundred entries); the <= 64 flattened nodes map one per
+// pools are a few hundred entries, so the C^2 compares are cheap once the
+// LDS reads are vectorised); the <= 64 flattened nodes map one per
 // lane of wave 0, where ancestor masks and depths come from six rounds of
 // pointer jumping over the parent links.
 #include "common.h"
@@ -42,6 +43,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     int32_t *__restrict__ o_depth, int32_t *__restrict__ o_pos, uint64_t *__restrict__ o_mask,
     int8_t *__restrict__ o_src, int32_t *__restrict__ err) {
   __shared__ float s_score[GRAFT_MAX_CAND];
+  __shared__ __attribute__((aligned(16))) uint64_t s_key[GRAFT_MAX_CAND];
   __shared__ int s_idx[GRAFT_MAX_CAND];  // kept flag, then flattened index or -1
   __shared__ int s_part[kThreads];
   __shared__ int s_np[GRAFT_MAX_NODES];
@@ -69,26 +71,39 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     return;
   }
 
-  for (int c = tid; c < C; c += kThreads) {
-    s_score[c] = cand_score[c0 + c];
-    int p = cand_parent[c0 + c];
-    bool pok = c == 0 ? p == -1 : (p >= 0 && p < c);
-    if (!pok) graft::raise_flag(err, GRAFT_ERR_PARENT);
-    int t = cand_token[c0 + c];
-    if (t < 0 || t >= V) graft::raise_flag(err, GRAFT_ERR_TOKEN);
+  // Ranking key of candidate c >= 1: (order(score) << 11) | (2047 - c), so
+  // "o ranks before c" (higher score, ties to the lower index) is exactly
+  // key_o > key_c.  The root's slot and the padding hold key 0, below every
+  // real key.  Counting uses the borrow bit of key_c - key_o: pure integer
+  // VALU work, no lane masks.
+  const int Cp = (C + 1) & ~1;
+  for (int c = tid; c < Cp; c += kThreads) {
+    uint64_t key = 0;
+    if (c < C) {
+      const float sc = cand_score[c0 + c];
+      int p = cand_parent[c0 + c];
+      bool pok = c == 0 ? p == -1 : (p >= 0 && p < c);
+      if (!pok) graft::raise_flag(err, GRAFT_ERR_PARENT);
+      int t = cand_token[c0 + c];
+      if (t < 0 || t >= V) graft::raise_flag(err, GRAFT_ERR_TOKEN);
+      s_score[c] = sc;
+      if (c > 0) key = (static_cast<uint64_t>(graft::float_order(sc)) << 11) | static_cast<uint64_t>(2047 - c);
+    }
+    s_key[c] = key;
   }
   __syncthreads();
 
   // keep the root and every candidate with fewer than bud-1 better others
   for (int c = tid; c < C; c += kThreads) {
-    int keep = 1;
-    if (c > 0) {
-      const float sc = s_score[c];
-      int better = 0;
-      for (int o = 1; o < C && better < bud - 1; ++o) better += graft::better(s_score[o], o, sc, c) ? 1 : 0;
-      keep = better < bud - 1;
+    const uint64_t kc = s_key[c];
+    uint64_t cnt = 0;
+#pragma unroll 8
+    for (int o2 = 0; o2 < Cp; o2 += 2) {
+      const ulonglong2 q = *reinterpret_cast<const ulonglong2 *>(&s_key[o2]);
+      cnt += (kc - q.x) >> 63;
+      cnt += (kc - q.y) >> 63;
     }
-    s_idx[c] = keep;
+    s_idx[c] = (c == 0 || cnt < static_cast<uint64_t>(bud - 1)) ? 1 : 0;
   }
   __syncthreads();
 

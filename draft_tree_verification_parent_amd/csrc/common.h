@@ -29,4 +29,11 @@ __device__ inline bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// Order-preserving 32-bit image of a float (larger float -> larger integer);
+// -0 is first folded into +0 so that the two compare equal.
+__device__ inline uint32_t float_order(float x) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 }  // namespace graft

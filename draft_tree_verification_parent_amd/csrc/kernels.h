@@ -15,5 +15,9 @@ struct TopkPlan {
 TopkPlan topk_plan(int M, int V, int k);
 int launch_topk(int M, int V, int k, const float *logits, int32_t *topk_id, float *topk_val, void *ws,
                 hipStream_t stream);
+// Merges `slices` sorted candidate lists of k (value, id) pairs per row.
+int launch_topk_merge(int M, int slices, int k, const uint64_t *part, int32_t *topk_id, float *topk_val,
+                      hipStream_t stream);
+size_t lmhead_fused_ws_bytes(int M, int V, int k);
 
 }  // namespace graft

@@ -84,6 +84,8 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
   __shared__ int s_key[kSlots];
   __shared__ int s_val[kSlots];
   __shared__ int s_tok[GRAFT_MAX_TEMPLATE_ROWS];
+  __shared__ int s_tp[GRAFT_MAX_TEMPLATE_ROWS];   // template parents, staged once
+  __shared__ int s_own[GRAFT_MAX_TEMPLATE_ROWS];  // owning request of each template row
   __shared__ signed char s_depth[GRAFT_MAX_TEMPLATE_ROWS];
   __shared__ int s_maxdepth;
   const int tid = threadIdx.x;
@@ -93,6 +95,10 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
     s_val[h] = -1;
   }
   if (tid == 0) s_maxdepth = 0;
+  for (int t = tid; t < tmpl_rows; t += kThreads) {
+    s_tp[t] = tparent[t];
+    s_own[t] = owner(toff, B, t);
+  }
   for (int b = tid; b < B_upd; b += kThreads) {
     int cap = upd_row_off[b + 1] - upd_row_off[b];
     if (upd_n[b] < 0 || upd_n[b] > cap) graft::raise_flag(err, GRAFT_ERR_CAPACITY);
@@ -107,13 +113,13 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
 
   // template depths (request-local parents must precede their child)
   for (int t = tid; t < tmpl_rows; t += kThreads) {
-    int b = owner(toff, B, t);
+    int b = s_own[t];
     int base = toff[b];
     int cur = t - base;
     int d = 1;
     bool ok = true;
     while (true) {
-      int p = tparent[base + cur];
+      int p = s_tp[base + cur];
       if (p < 0) break;
       if (p >= cur) {
         ok = false;
@@ -147,9 +153,9 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
   for (int level = 1; level <= maxd; ++level) {
     for (int t = tid; t < tmpl_rows; t += kThreads) {
       if (s_depth[t] != level) continue;
-      int b = owner(toff, B, t);
+      int b = s_own[t];
       int base = toff[b];
-      int p = tparent[t];
+      int p = s_tp[t];
       int src = p < 0 ? root_token[b] : s_tok[base + p];
       int rank = trank[t];
       int tok = -1;

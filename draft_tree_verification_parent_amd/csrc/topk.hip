@@ -11,96 +11,28 @@
 //     each wavefront merges its 64 lists with k rounds of a (value, id)
 //     butterfly max, and wave 0 merges the four wave results; k candidates
 //     per (row, slice) go to the workspace.
-//  2. one wavefront per row merges the slices' candidates the same way.
+//  2. one workgroup per row merges the slices' candidates the same way.
 // The (value desc, id asc) order is total on non-NaN values, so the result
 // does not depend on how the vocabulary is split.
 #include <climits>
 
 #include "common.h"
 #include "kernels.h"
+#include "topk_list.h"
 
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kSliceQuantum = 1024;  // 256 threads x float4
 
-template <int K>
-struct TopList {
-  float v[K];
-  int id[K];
-  __device__ void init() {
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      v[j] = -INFINITY;
-      id[j] = INT_MAX;
-    }
-  }
-  __device__ void insert(float x, int i) {
-    if (!graft::better(x, i, v[K - 1], id[K - 1])) return;
-    v[K - 1] = x;
-    id[K - 1] = i;
-#pragma unroll
-    for (int j = K - 1; j > 0; --j) {
-      const bool sw = graft::better(v[j], id[j], v[j - 1], id[j - 1]);
-      const float tv = v[j - 1];
-      const int ti = id[j - 1];
-      v[j - 1] = sw ? v[j] : tv;
-      id[j - 1] = sw ? id[j] : ti;
-      v[j] = sw ? tv : v[j];
-      id[j] = sw ? ti : id[j];
-    }
-  }
-  __device__ void pop_front() {
-#pragma unroll
-    for (int j = 0; j < K - 1; ++j) {
-      v[j] = v[j + 1];
-      id[j] = id[j + 1];
-    }
-    v[K - 1] = -INFINITY;
-    id[K - 1] = INT_MAX;
-  }
-};
-
-// Best (value, id) over the 64 lanes; every lane gets the result.
-__device__ inline void wave_best(float &bv, int &bi) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    if (graft::better(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
-    }
-  }
-}
-
-// k rounds of extraction from per-lane sorted lists; lane j < k returns the
-// j-th best in (out_v, out_i).
-template <int K>
-__device__ void wave_extract(TopList<K> &L, int k, float &out_v, int &out_i) {
-  const int lane = threadIdx.x & 63;
-  out_v = -INFINITY;
-  out_i = INT_MAX;
-  for (int j = 0; j < k; ++j) {
-    float bv = L.v[0];
-    int bi = L.id[0];
-    wave_best(bv, bi);
-    if (L.id[0] == bi && L.v[0] == bv) L.pop_front();
-    if (lane == j) {
-      out_v = bv;
-      out_i = bi;
-    }
-  }
-}
+using graft::TopKeys;
 
 template <int K>
 __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__restrict__ logits, int V, int k,
-                                                              int slice_len, float *__restrict__ part_v,
-                                                              int *__restrict__ part_i,
+                                                              int slice_len, uint64_t *__restrict__ part,
                                                               int32_t *__restrict__ out_id,
                                                               float *__restrict__ out_val) {
-  __shared__ float s_v[4][GRAFT_MAX_K];
-  __shared__ int s_i[4][GRAFT_MAX_K];
+  __shared__ uint64_t s_k[4][GRAFT_MAX_K];
   const int s = blockIdx.x;
   const int S = gridDim.x;
   const int m = blockIdx.y;
@@ -111,63 +43,78 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
   const int lo = s * slice_len;
   const int hi = lo + slice_len < V ? lo + slice_len : V;
 
-  TopList<K> L;
+  TopKeys<K> L;
   L.init();
   if ((V & 3) == 0) {
     for (int c = lo + tid * 4; c < hi; c += kThreads * 4) {
       const float4 x = *reinterpret_cast<const float4 *>(row + c);
-      L.insert(x.x, c);
-      L.insert(x.y, c + 1);
-      L.insert(x.z, c + 2);
-      L.insert(x.w, c + 3);
+      L.insert(graft::rank_key(x.x, c));
+      L.insert(graft::rank_key(x.y, c + 1));
+      L.insert(graft::rank_key(x.z, c + 2));
+      L.insert(graft::rank_key(x.w, c + 3));
     }
   } else {
-    for (int c = lo + tid; c < hi; c += kThreads) L.insert(row[c], c);
+    for (int c = lo + tid; c < hi; c += kThreads) L.insert(graft::rank_key(row[c], c));
   }
 
-  float rv;
-  int ri;
-  wave_extract<K>(L, k, rv, ri);
-  if (lane < k) {
-    s_v[wave][lane] = rv;
-    s_i[wave][lane] = ri;
-  }
+  uint64_t r = graft::wave_extract<K>(L, k);
+  if (lane < k) s_k[wave][lane] = r;
   __syncthreads();
   if (wave == 0) {
-    TopList<K> M;
-    M.init();
-    if (lane < 4 * k) M.insert(s_v[lane / k][lane % k], s_i[lane / k][lane % k]);
-    wave_extract<K>(M, k, rv, ri);
+    TopKeys<K> M2;
+    M2.init();
+    if (lane < 4 * k) M2.insert(s_k[lane / k][lane % k]);
+    r = graft::wave_extract<K>(M2, k);
     if (lane < k) {
       if (S == 1) {
-        out_id[static_cast<size_t>(m) * k + lane] = ri == INT_MAX ? 0 : ri;
-        if (out_val) out_val[static_cast<size_t>(m) * k + lane] = rv;
+        out_id[static_cast<size_t>(m) * k + lane] = r ? graft::key_id(r) : 0;
+        if (out_val) out_val[static_cast<size_t>(m) * k + lane] = r ? graft::key_value(r) : -INFINITY;
       } else {
-        const size_t o = (static_cast<size_t>(m) * S + s) * k + lane;
-        part_v[o] = rv;
-        part_i[o] = ri;
+        part[(static_cast<size_t>(m) * S + s) * k + lane] = r;
       }
     }
   }
 }
 
+// One 256-thread workgroup per row: each thread ranks ~1/256 of the row's
+// candidates (loads batched 8 at a time so their latencies overlap), each
+// wavefront extracts its k best, and wave 0 merges the four wave results.
 template <int K>
-__global__ __launch_bounds__(64) void topk_merge_kernel(int S, int k, const float *__restrict__ part_v,
-                                                        const int *__restrict__ part_i,
-                                                        int32_t *__restrict__ out_id,
-                                                        float *__restrict__ out_val) {
+__global__ __launch_bounds__(kThreads) void topk_merge_kernel(int S, int k, const uint64_t *__restrict__ part,
+                                                              int32_t *__restrict__ out_id,
+                                                              float *__restrict__ out_val) {
+  __shared__ uint64_t s_k[4][GRAFT_MAX_K];
   const int m = blockIdx.x;
-  const int lane = threadIdx.x;
-  const size_t base = static_cast<size_t>(m) * S * k;
-  TopList<K> L;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const uint64_t *row = part + static_cast<size_t>(m) * S * k;
+  const int n = S * k;
+  TopKeys<K> L;
   L.init();
-  for (int c = lane; c < S * k; c += 64) L.insert(part_v[base + c], part_i[base + c]);
-  float rv;
-  int ri;
-  wave_extract<K>(L, k, rv, ri);
-  if (lane < k) {
-    out_id[static_cast<size_t>(m) * k + lane] = ri == INT_MAX ? 0 : ri;
-    if (out_val) out_val[static_cast<size_t>(m) * k + lane] = rv;
+  constexpr int BATCH = 8;
+  for (int c0 = 0; c0 < n; c0 += kThreads * BATCH) {
+    uint64_t x[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int c = c0 + j * kThreads + tid;
+      x[j] = c < n ? row[c] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) L.insert(x[j]);
+  }
+  uint64_t r = graft::wave_extract<K>(L, k);
+  if (lane < k) s_k[wave][lane] = r;
+  __syncthreads();
+  if (wave == 0) {
+    TopKeys<K> M2;
+    M2.init();
+    if (lane < 4 * k) M2.insert(s_k[lane / k][lane % k]);
+    r = graft::wave_extract<K>(M2, k);
+    if (lane < k) {
+      out_id[static_cast<size_t>(m) * k + lane] = r ? graft::key_id(r) : 0;
+      if (out_val) out_val[static_cast<size_t>(m) * k + lane] = r ? graft::key_value(r) : -INFINITY;
+    }
   }
 }
 
@@ -185,30 +132,33 @@ TopkPlan topk_plan(int M, int V, int k) {
   per = (per + kSliceQuantum - 1) / kSliceQuantum * kSliceQuantum;
   p.slice_len = per;
   p.slices = (V + per - 1) / per;
-  p.ws_bytes = p.slices > 1 ? static_cast<size_t>(M) * p.slices * k * (sizeof(float) + sizeof(int)) : 0;
+  p.ws_bytes = p.slices > 1 ? static_cast<size_t>(M) * p.slices * k * sizeof(uint64_t) : 0;
   return p;
 }
 
 int launch_topk(int M, int V, int k, const float *logits, int32_t *topk_id, float *topk_val, void *ws,
                 hipStream_t stream) {
   const TopkPlan p = topk_plan(M, V, k);
-  float *part_v = static_cast<float *>(ws);
-  int *part_i = reinterpret_cast<int *>(part_v + static_cast<size_t>(M) * p.slices * k);
+  uint64_t *part = static_cast<uint64_t *>(ws);
   dim3 grid(p.slices, M);
-  if (k <= 8) {
-    hipLaunchKernelGGL(topk_slice_kernel<8>, grid, dim3(kThreads), 0, stream, logits, V, k, p.slice_len,
-                       part_v, part_i, topk_id, topk_val);
-    if (p.slices > 1)
-      hipLaunchKernelGGL(topk_merge_kernel<8>, dim3(M), dim3(64), 0, stream, p.slices, k, part_v, part_i,
-                         topk_id, topk_val);
-  } else {
-    hipLaunchKernelGGL(topk_slice_kernel<16>, grid, dim3(kThreads), 0, stream, logits, V, k, p.slice_len,
-                       part_v, part_i, topk_id, topk_val);
-    if (p.slices > 1)
-      hipLaunchKernelGGL(topk_merge_kernel<16>, dim3(M), dim3(64), 0, stream, p.slices, k, part_v, part_i,
-                         topk_id, topk_val);
-  }
+  if (k <= 8)
+    hipLaunchKernelGGL(topk_slice_kernel<8>, grid, dim3(kThreads), 0, stream, logits, V, k, p.slice_len, part,
+                       topk_id, topk_val);
+  else
+    hipLaunchKernelGGL(topk_slice_kernel<16>, grid, dim3(kThreads), 0, stream, logits, V, k, p.slice_len, part,
+                       topk_id, topk_val);
+  if (p.slices > 1) return launch_topk_merge(M, p.slices, k, part, topk_id, topk_val, stream);
   return check_launch("topk");
+}
+
+int launch_topk_merge(int M, int slices, int k, const uint64_t *part, int32_t *topk_id, float *topk_val,
+                      hipStream_t stream) {
+  if (k <= 8)
+    hipLaunchKernelGGL(topk_merge_kernel<8>, dim3(M), dim3(kThreads), 0, stream, slices, k, part, topk_id, topk_val);
+  else
+    hipLaunchKernelGGL(topk_merge_kernel<16>, dim3(M), dim3(kThreads), 0, stream, slices, k, part, topk_id,
+                       topk_val);
+  return check_launch("topk merge");
 }
 
 }  // namespace graft

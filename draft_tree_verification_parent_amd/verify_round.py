@@ -8,9 +8,11 @@ section 6, second level):
   2. graft_build_tree            -- select, append retrieved nodes, flatten,
                                     depth / positions / mask;
   3. graft_tree_attention        -- one tree-masked attention layer;
-  4. graft_lmhead_topk           -- logits (materialised) ...
-  5. graft_lmhead_topk           -- ... and their per-row top-k;
-  6. graft_accept                -- deepest accepted path and bonus token.
+  4. graft_lmhead_topk           -- logits and their per-row top-k, fused
+                                    (logits never written) or, with
+                                    fused=False, as two calls that
+                                    materialise the logits;
+  5. graft_accept                -- deepest accepted path and bonus token.
 The next round's update reads this round's tree tokens and top-k ids.
 
 Device memory comes from torch; every computation runs in libgraft.
@@ -23,7 +25,8 @@ import torch
 from . import api
 from ._native import TREE_PRUNE, TREE_STATIC_REPLACE
 
-STEPS = ("update_retrieve", "build_tree", "tree_attention", "lmhead", "topk", "accept")
+STEPS_FUSED = ("update_retrieve", "build_tree", "tree_attention", "lmhead_topk", "accept")
+STEPS_SPLIT = ("update_retrieve", "build_tree", "tree_attention", "lmhead", "topk", "accept")
 
 
 def _i32(x, dev):
@@ -36,8 +39,10 @@ def _bf16(bits, dev):
 
 
 class VerifyRound:
-    def __init__(self, ri, w_bits=None, device="cuda", dmax: int = 8):
+    def __init__(self, ri, w_bits=None, device="cuda", dmax: int = 8, fused: bool = True):
         dev = torch.device(device)
+        self.fused = fused
+        self.steps = STEPS_FUSED if fused else STEPS_SPLIT
         wl = ri.wl
         self.ri, self.wl, self.dev = ri, wl, dev
         B, N, k, V = ri.B, ri.N, ri.k, ri.V
@@ -97,7 +102,7 @@ class VerifyRound:
 
         self.w = _bf16(w_bits, dev) if w_bits is not None else None
         self.hidden = None
-        self.logits = torch.empty(rows, V, dtype=torch.float32, device=dev)
+        self.logits = None if fused else torch.empty(rows, V, dtype=torch.float32, device=dev)
         self.topk_id = z(rows, k)
         self.topk_val = torch.empty(rows, k, dtype=torch.float32, device=dev)
         tkb = api.graft_lmhead_topk_workspace_bytes(rows, V, k)
@@ -140,6 +145,10 @@ class VerifyRound:
     def step_lmhead(self):
         api.graft_lmhead_topk(self.rows, self.wl.H, self.V, 0, self.hidden, self.w, self.logits)
 
+    def step_lmhead_topk(self):
+        api.graft_lmhead_topk(self.rows, self.wl.H, self.V, self.k, self.hidden, self.w, None,
+                              self.topk_id, self.topk_val, self.topk_ws)
+
     def step_topk(self):
         api.graft_lmhead_topk(self.rows, self.wl.H, self.V, self.k, None, None, self.logits,
                               self.topk_id, self.topk_val, self.topk_ws)
@@ -151,7 +160,7 @@ class VerifyRound:
     def run(self, events=None):
         """Enqueue one round.  `events`, if given, is a dict step -> list that
         receives (start, end) torch.cuda.Event pairs recorded on the stream."""
-        for name in STEPS:
+        for name in self.steps:
             fn = getattr(self, "step_" + name)
             if events is None:
                 fn()

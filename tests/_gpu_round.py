@@ -33,13 +33,13 @@ def prepared(cfg: int):
     return wl, ri, w, ts, hidden
 
 
-def run_gpu_round(cfg: int):
+def run_gpu_round(cfg: int, fused: bool = False):
     import torch
 
     from draft_tree_verification_parent_amd.verify_round import VerifyRound
     wl, ri, w, ts, hidden = prepared(cfg)
-    say(f"[gpu] cfg {cfg}: one round through libgraft")
-    vr = VerifyRound(ri, w)
+    say(f"[gpu] cfg {cfg}: one round through libgraft ({'fused' if fused else 'split'} lm-head/top-k)")
+    vr = VerifyRound(ri, w, fused=fused)
     vr.set_hidden(hidden)
     vr.run()
     torch.cuda.synchronize()

@@ -74,7 +74,7 @@ def test_host_argument_validation_launches_nothing(native):
     # lm-head / top-k
     assert L.graft_lmhead_topk(4, 256, 100, 17, 1, 1, 1, 1, None, 1, 1 << 20, None) == E
     assert L.graft_lmhead_topk(4, 100, 100, 4, 1, 1, 1, 1, None, 1, 1 << 20, None) == E
-    assert L.graft_lmhead_topk(4, 256, 100, 4, 1, 1, None, 1, None, 1, 1 << 20, None) == U
+    assert L.graft_lmhead_topk(4, 256, 100, 0, 1, 1, None, None, None, None, 0, None) == E
     assert L.graft_lmhead_topk(4, 256, 100, 4, None, None, None, 1, None, 1, 1 << 20, None) == E
     assert L.graft_lmhead_topk(4, 256, 100, 200, None, None, 1, 1, None, 1, 1 << 20, None) == E
     assert L.graft_lmhead_topk(0, 256, 100, 4, None, None, 1, 1, None, None, 0, None) == 0

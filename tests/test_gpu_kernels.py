@@ -108,6 +108,28 @@ def test_lmhead_then_topk_in_one_call(api):
     assert np.array_equal(ids.cpu().numpy(), eid)
 
 
+@pytest.mark.parametrize("M,H,V,k", [(60, 4096, 128256, 8), (130, 320, 1001, 16), (1, 64, 5, 3),
+                                     (64, 256, 129, 10)])
+def test_fused_lmhead_topk_equals_split(api, M, H, V, k):
+    """Fused mode ranks exactly the logits the split mode writes."""
+    say(f"[fused lmhead+topk] M={M} H={H} V={V} k={k}")
+    r = np.random.default_rng(M * 3 + V)
+    h = f32_to_bf16_bits(r.standard_normal((M, H)).astype(np.float32))
+    w = f32_to_bf16_bits((0.02 * r.standard_normal((V, H))).astype(np.float32))
+    hd, wd = dev_bf16(h), dev_bf16(w)
+    logits = torch.empty(M, V, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(api.graft_lmhead_topk_workspace_bytes(M, V, k), 1), dtype=torch.uint8, device="cuda")
+    api.graft_lmhead_topk(M, H, V, 0, hd, wd, logits)
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    vals = torch.empty(M, k, dtype=torch.float32, device="cuda")
+    api.graft_lmhead_topk(M, H, V, k, hd, wd, None, ids, vals, ws)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    eid, ev = OT.topk(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), eid)
+    assert np.array_equal(vals.cpu().numpy(), ev)
+
+
 # ----------------------------------------------------------------------------- accept
 
 def _accept_gpu(api, n, row_off, parent, token, argmax):

@@ -109,6 +109,16 @@ def test_round_parity(cfg):
         assert acc_path[b].tolist() == expect
     say(f"[accept] cfg {cfg}: accepted lengths {lens[:8]}")
 
+    # the fused lm-head + top-k runs the same accumulation: identical ids,
+    # values and acceptance, without materialising the logits
+    del vr
+    _, _, _, _, _, vf = run_gpu_round(cfg, fused=True)
+    assert vf.err.item() == 0
+    assert np.array_equal(vf.topk_id.cpu().numpy(), topk_id)
+    assert np.array_equal(vf.topk_val.cpu().numpy(), topk_val)
+    assert vf.acc_len.cpu().numpy().tolist() == lens
+    assert vf.bonus.cpu().numpy().tolist() == bonus
+
 
 def test_end_to_end_argmax_where_margin_is_clear():
     """Rows whose fp64 top-1/top-2 logit margin is far above the lm-head's
