@@ -111,6 +111,7 @@ class VerifyRound:
         self.acc_len = z(B)
         self.acc_path = z(B, 64)
         self.bonus = z(B)
+        self.graph = None
 
     def set_hidden(self, hidden_bits):
         self.hidden = _bf16(hidden_bits.reshape(self.rows, self.wl.H), self.dev)
@@ -171,6 +172,23 @@ class VerifyRound:
                 fn()
                 e1.record()
                 events.setdefault(name, []).append((e0, e1))
+
+    def capture(self):
+        """Record one round as a HIP graph with the update pointers as they
+        stand (call chain_update() first for steady-state rounds: every round
+        then reads the previous round's outputs from the same buffers).
+        Nothing runs during capture; replay() issues one round.  The round
+        has no memset nodes and no host synchronisation, so it replays as
+        recorded."""
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            self.run()
+        self.graph = g
+        return g
+
+    def replay(self):
+        self.graph.replay()
 
     def tree_host(self):
         """Built tree copied to the host (synchronises)."""

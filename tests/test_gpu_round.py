@@ -144,3 +144,36 @@ def test_end_to_end_argmax_where_margin_is_clear():
     assert clear.sum() >= 4
     assert np.array_equal(gpu_arg[rows][clear], arg[clear])
     say(f"[e2e] {int(clear.sum())} of {len(rows)} rows have a clear margin; all match")
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_graph_replay_matches_eager(cfg):
+    """A round captured as a HIP graph and replayed several times (with
+    unrelated eager work and synchronisations between replays) gives, round
+    after round, exactly what the same rounds give issued eagerly."""
+    _need_gpu()
+    from draft_tree_verification_parent_amd.verify_round import VerifyRound
+
+    from _gpu_round import prepared
+    wl, ri, w, ts, hidden = prepared(cfg)
+    eager = VerifyRound(ri, w, fused=True)
+    graph = VerifyRound(ri, w, fused=True)
+    for vr in (eager, graph):
+        vr.set_hidden(hidden)
+        vr.run()
+        vr.chain_update()
+    graph.capture()
+    outs = ("table", "ret_token", "n_out", "parent", "token", "depth", "pos", "mask", "src",
+            "attn_out", "lse", "topk_id", "topk_val", "acc_len", "acc_path", "bonus", "err")
+    for rnd in range(4):
+        eager.run()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        del junk
+        for name in outs:
+            a, b = getattr(eager, name), getattr(graph, name)
+            assert torch.equal(a, b), f"round {rnd + 2}: {name} differs between replay and eager"
+    say(f"[graph] cfg {cfg}: 4 replays identical to eager rounds")
