@@ -202,8 +202,9 @@ def main():
     traffic = measured_traffic(wkey)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": (f"lmhead_kernel<{128 if H % 128 == 0 else 64},true,{8 if ri.k <= 8 else 16}> + "
-                           f"topk_merge_kernel<{8 if ri.k <= 8 else 16}> (one graft_lmhead_topk call)"),
+                "kernel": (f"lmhead_packed_kernel<true,{8 if ri.k <= 8 else 16}> + "
+                           f"topk_merge_kernel<{8 if ri.k <= 8 else 16}> (one graft_lmhead_topk call, "
+                           f"packed weights)"),
                 "algorithmic_bytes_per_launch": lm_bytes,
                 "mfma_frac": round(lm_flops / lm_s / 1e12 / MFMA_BF16_PEAK_TFS, 4)}
     # secondary kernels, same convention (algorithmic bytes / measured time)

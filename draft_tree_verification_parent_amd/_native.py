@@ -25,7 +25,9 @@ SIGNATURES = {
     "graft_tree_attention": (c_int, [c_int, c_int, c_int, c_int, c_float, P, P, P, P, c_int64,
                                      P, c_int, P, c_int, P, P, P, P, P, c_size_t, P, P]),
     "graft_lmhead_topk_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),
-    "graft_lmhead_topk": (c_int, [c_int, c_int, c_int, c_int, P, P, P, P, P, P, c_size_t, P]),
+    "graft_lmhead_topk": (c_int, [c_int, c_int, c_int, c_int, P, P, c_int, P, P, P, P, c_size_t, P]),
+    "graft_lmhead_pack_bytes": (c_size_t, [c_int, c_int]),
+    "graft_lmhead_pack": (c_int, [c_int, c_int, P, P, P]),
     "graft_accept": (c_int, [c_int, P, P, P, P, P, c_int, P, P, P, P, P]),
     "graft_make_template": (c_int, [c_int, c_int, c_int, P, P]),
     "graft_stage_budget": (c_int, [c_int, P, P]),
@@ -35,6 +37,7 @@ GRAFT_OK, GRAFT_EINVAL, GRAFT_EUNSUPPORTED, GRAFT_EHIP = 0, -1, -2, -3
 ERR_TOKEN, ERR_PARENT, ERR_NOT_CLOSED, ERR_CAPACITY, ERR_RANK = 1, 2, 4, 8, 16
 SRC_ROOT, SRC_DRAFT, SRC_RETRIEVED, SRC_REPLACED = 0, 1, 2, 3
 TREE_PRUNE, TREE_STATIC_REPLACE = 0, 1
+W_ROWMAJOR, W_PACKED = 0, 1
 MAX_NODES, MAX_K = 64, 16
 
 

@@ -90,11 +90,25 @@ def graft_lmhead_topk_workspace_bytes(M, V, k):
 
 
 def graft_lmhead_topk(M, H, V, k, hidden, w, logits, topk_id=None, topk_val=None, ws=None,
-                      stream=None):
+                      stream=None, w_layout=N.W_ROWMAJOR):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     return call("graft_lmhead_topk", int(M), int(H), int(V), int(k), _p(hidden, "bf16", "hidden"),
-                _p(w, "bf16", "w"), _p(logits, "f32", "logits"), _p(topk_id, "i32", "topk_id"),
+                _p(w, "bf16", "w"), int(w_layout), _p(logits, "f32", "logits"), _p(topk_id, "i32", "topk_id"),
                 _p(topk_val, "f32", "topk_val"), None if ws is None else ws.data_ptr(), ws_bytes,
+                _s(stream))
+
+
+def graft_lmhead_pack_bytes(V, H):
+    return int(N.lib().graft_lmhead_pack_bytes(V, H))
+
+
+def graft_lmhead_pack(V, H, w, w_packed, stream=None):
+    """Rewrite the row-major lm-head weight w [V, H] into the packed layout
+    (w_packed: bf16 device tensor of graft_lmhead_pack_bytes(V, H) bytes)."""
+    need = graft_lmhead_pack_bytes(V, H)
+    if w_packed.numel() * w_packed.element_size() < need:
+        raise ValueError(f"w_packed holds {w_packed.numel() * w_packed.element_size()} bytes < {need}")
+    return call("graft_lmhead_pack", int(V), int(H), _p(w, "bf16", "w"), _p(w_packed, "bf16", "w_packed"),
                 _s(stream))
 
 

@@ -7,25 +7,29 @@
 //
 // With M = tree nodes (tens) and V x H = 0.5-0.8 G weights, this is a
 // weight-streaming product bound by HBM (about 60 flop per weight byte).
-// Each workgroup owns BV = 32 * WAVES vocabulary rows and BM = 64 hidden rows:
-//  * W is read once, straight from HBM into MFMA A-operand registers
-//    (16 contiguous bytes per lane); the next K chunk's loads are issued
-//    before the current chunk's MFMAs;
-//  * the hidden states, shared by every workgroup, are staged through a
-//    double-buffered LDS tile in K chunks of 256 and read as B operands; the
-//    next chunk's hidden loads are issued *before* the next W loads, so that
-//    waiting for them (vector-memory counters retire in order) never waits
-//    for W;
-//  * V_MFMA_F32_16X16X32_BF16 computes 16 vocabulary rows x 16 hidden rows;
-//    each lane ends with 4 consecutive vocabulary entries of one row.
-// Fused top-k: the 64 x BV logit tile goes through LDS, WAVES threads per row
-// each rank 32 entries into a sorted register list, the lists of a row are
-// merged with xor shuffles, and k (value, id) candidates per (row, tile) are
-// written; a second kernel merges the tiles (same (value desc, id asc)
-// order, so the result does not depend on the split).
-// Tiles are ordered so that the M tiles of one V tile are consecutive on one
-// XCD (workgroups are dealt round-robin to the 8 XCDs), which keeps repeated
-// W tiles in that XCD's L2 when M > 64.
+// V_MFMA_F32_16X16X32_BF16 computes 16 vocabulary rows x 16 hidden rows.
+//
+// Two weight layouts:
+//  * packed (graft_lmhead_pack, done once when the weights are loaded): W
+//    is cut into stage images of 128 vocabulary rows x 128 hidden columns
+//    (32 KB), stored tile by tile, chunk by chunk, so a workgroup's whole
+//    weight stream is one contiguous, linearly read region.  Inside an image
+//    row r keeps its 16-byte pieces in XOR-swizzled order (piece p at slot
+//    p ^ (r & 15)), so 16 lanes reading one MFMA fragment column hit all
+//    LDS banks once.  A persistent grid (one 144 KB workgroup per CU) copies
+//    images HBM -> LDS with global_load_lds_dwordx4 (LDS DMA: no registers,
+//    in a 3-stage ring that runs across tile boundaries), stages the hidden
+//    chunk the same way, and reads both MFMA operands from LDS.
+//    Linear reads reach about 7.2 TB/s on MI355X where row-major tiles
+//    (256-byte runs per row) stall near 5.6 TB/s.
+//  * row-major W [V, H]: W read straight from HBM into MFMA operand
+//    registers (ping-pong buffers), the hidden chunk double-buffered in LDS.
+// Fused top-k: each logit tile goes through LDS and 4 threads per row rank
+// 32 entries each into sorted register lists of 64-bit (value, id) keys; k
+// keys per (row, list owner) are written and a second kernel merges them
+// (the (value desc, id asc) order is total, so the result does not depend
+// on the split).  In the packed path the lists persist across a
+// workgroup's tiles, so the merge reads one list per (row, workgroup).
 #include <climits>
 #include <type_traits>
 
@@ -215,6 +219,235 @@ __global__ __launch_bounds__(kThreads, 4) void lmhead_kernel(int M, int H, int V
   }
 }
 
+// ---------------------------------------------------------------- packed W
+constexpr int PK_BV = 128;                  // vocabulary rows per tile
+constexpr int PK_KC = 128;                  // hidden columns per chunk
+constexpr int PK_NS = 3;                    // LDS ring stages
+constexpr int PK_WB = PK_BV * PK_KC * 2;    // 32 KB stage image of W
+constexpr int PK_HB = BM * PK_KC * 2;       // 16 KB hidden chunk
+constexpr int PK_SB = PK_WB + PK_HB;        // one ring stage
+constexpr int PK_WI = PK_WB / 1024 / kWaves;  // W DMA instructions per wave per stage (8)
+constexpr int PK_HI = PK_HB / 1024 / kWaves;  // hidden DMA instructions per wave per stage (4)
+constexpr int PK_GRID = 256;                // persistent workgroups (one per MI355X CU)
+constexpr int PK_TSTR = PK_BV + 4;          // floats per row of the staged logit tile
+static_assert(BM * PK_TSTR * 4 <= PK_SB, "logit tile must fit in one ring stage");
+
+// Image (tile t, chunk c) at byte ((t * nch + c) * PK_WB); inside it, byte
+// r * 256 + p * 16 holds W[128 t + r][128 c + 8 (p ^ (r & 15)) .. + 8], zero
+// for rows >= V.  One thread per 16-byte piece.
+__global__ __launch_bounds__(256) void lmhead_pack_kernel(int H, int V, const graft_bf16 *__restrict__ w,
+                                                          u32x4 *__restrict__ out, size_t pieces) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= pieces) return;
+  const int nch = H / PK_KC;
+  const int p = static_cast<int>(i & 15);
+  const int r = static_cast<int>((i >> 4) & (PK_BV - 1));
+  const size_t img = i >> 11;  // 2048 pieces per image
+  const int c = static_cast<int>(img % nch);
+  const size_t row = (img / nch) * PK_BV + r;
+  const int col = c * PK_KC + 8 * (p ^ (r & 15));
+  out[i] = row < static_cast<size_t>(V) ? *reinterpret_cast<const u32x4 *>(w + row * H + col) : zero4();
+}
+
+// 16-byte LDS DMA: lane l's 16 bytes from sbase + voff land at LDS byte
+// lds + 16 l.  Issued through asm so the compiler does not serialise the
+// ring with conservative waits; completion is tracked by hand with vmcnt.
+__device__ inline void lds_dma16(unsigned lds, const void *sbase, unsigned voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt" ::"s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+__device__ inline void lds_dma16_cached(unsigned lds, const void *sbase, unsigned voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+// Wait until at most N of this wave's DMAs are outstanding and every LDS
+// access of this wave has completed, then meet the other waves.
+template <int N>
+__device__ inline void ring_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Which (m tile, tile stream) a persistent workgroup serves.  With T m-tiles
+// and T <= 32, the 32 workgroups of one XCD (workgroups are dealt
+// round-robin to the 8 XCDs) form 32/T groups of T: the T workgroups of a
+// group take the same vocabulary tiles at the same time with different m
+// tiles, so a W image fetched from HBM is re-read from that XCD's L2.
+struct PkMap {
+  int tm, stream, streams;
+};
+__device__ __host__ inline PkMap pk_map(int block, int T) {
+  PkMap r;
+  if (T <= 32) {
+    const int groups = 32 / T;
+    const int xcd = block % 8, slot = block / 8;
+    const int gi = slot / T;
+    r.tm = slot % T;
+    r.streams = groups * 8;
+    r.stream = gi < groups ? gi * 8 + xcd : -1;
+  } else {
+    r.streams = PK_GRID / T;
+    r.tm = block % T;
+    r.stream = block / T < r.streams ? block / T : -1;
+  }
+  return r;
+}
+
+template <bool FUSED, int K>
+__global__ __launch_bounds__(kThreads, 1) void lmhead_packed_kernel(int M, int H, int V, int k,
+                                                                  const graft_bf16 *__restrict__ hidden,
+                                                                  const unsigned char *__restrict__ wpk,
+                                                                  float *__restrict__ logits,
+                                                                  uint64_t *__restrict__ part_out, int tiles_m,
+                                                                  int tiles_v) {
+  __shared__ __attribute__((aligned(1024))) unsigned char sm[PK_NS * PK_SB];
+  const PkMap map = pk_map(blockIdx.x, tiles_m);
+  if (map.stream < 0) return;
+  const int S = map.streams;
+  const int m0 = map.tm * BM;
+  const int nch = H / PK_KC;
+  const int items = map.stream < tiles_v ? (tiles_v - map.stream + S - 1) / S : 0;
+  const int Q = items * nch;  // chunks this workgroup streams
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // LDS byte address of the ring (the M0 base of the DMAs)
+  const unsigned sbase = static_cast<unsigned>(reinterpret_cast<size_t>((__attribute__((address_space(3))) void *)sm));
+
+  // loop-invariant DMA source offsets: W images are copied linearly; hidden
+  // row r (clamped to M - 1) lands swizzled like the images
+  unsigned wo[PK_WI], ho[PK_HI];
+#pragma unroll
+  for (int i = 0; i < PK_WI; ++i) wo[i] = ((wave * PK_WI + i) * 64 + lane) * 16;
+#pragma unroll
+  for (int i = 0; i < PK_HI; ++i) {
+    const int r = 4 * (wave * PK_HI + i) + (lane >> 4);
+    const int m = min(m0 + r, M - 1);
+    ho[i] = static_cast<unsigned>(m) * H * 2 + (((lane & 15) ^ (r & 15)) * 16);
+  }
+  auto issue = [&](int q) {
+    const int st = q % PK_NS;
+    const int tv = map.stream + (q / nch) * S;
+    const int c = q - (q / nch) * nch;
+    const unsigned char *wsrc = wpk + (static_cast<size_t>(tv) * nch + c) * PK_WB;
+    const unsigned char *hsrc = reinterpret_cast<const unsigned char *>(hidden) + c * PK_KC * 2;
+    const unsigned wl = sbase + st * PK_SB + wave * PK_WI * 1024;
+    const unsigned hl = sbase + st * PK_SB + PK_WB + wave * PK_HI * 1024;
+#pragma unroll
+    for (int i = 0; i < PK_HI; ++i) lds_dma16_cached(hl + i * 1024, hsrc, ho[i]);
+#pragma unroll
+    for (int i = 0; i < PK_WI; ++i) lds_dma16(wl + i * 1024, wsrc, wo[i]);
+  };
+
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  graft::TopKeys<K> L;
+  L.init();
+
+  if (Q > 0) issue(0);
+  if (Q > 1) issue(1);
+  for (int q = 0; q < Q; ++q) {
+    // chunk q has landed once only chunk q + 1's DMAs may still be in flight
+    if (q + 1 < Q) ring_barrier<PK_WI + PK_HI>();
+    else ring_barrier<0>();
+    if (q + 2 < Q) issue(q + 2);  // into the stage chunk q - 1 used
+    const unsigned char *ws = sm + (q % PK_NS) * PK_SB;
+    const unsigned char *hs = ws + PK_WB;
+#pragma unroll
+    for (int s = 0; s < PK_KC / 32; ++s) {
+      const int P = s * 4 + g;  // 16-byte piece of the lane's 8 k values
+      bf16x8 a[2], bh[4];
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb)
+        a[vb] = *reinterpret_cast<const bf16x8 *>(ws + (wave * 32 + vb * 16 + l16) * 256 + (P ^ l16) * 16);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        bh[mb] = *reinterpret_cast<const bf16x8 *>(hs + (mb * 16 + l16) * 256 + (P ^ l16) * 16);
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          acc[vb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[vb], bh[mb], acc[vb][mb], 0, 0, 0);
+    }
+    if (q - (q / nch) * nch != nch - 1) continue;
+
+    // ---- tile done: stage the 64 x 128 logits in this chunk's ring stage
+    // (free until chunk q + 3 is issued, after the next ring barrier)
+    const int v0 = (map.stream + (q / nch) * S) * PK_BV;
+    float *s_t = reinterpret_cast<float *>(sm + (q % PK_NS) * PK_SB);
+    __syncthreads();  // every wave is done reading the stage
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb) {
+        *reinterpret_cast<f32x4 *>(&s_t[(mb * 16 + l16) * PK_TSTR + wave * 32 + vb * 16 + 4 * g]) = acc[vb][mb];
+        acc[vb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    __syncthreads();
+    if constexpr (FUSED) {
+      // 4 consecutive threads per row, 32 entries each, into the persistent
+      // lists.  An entry whose key is not above the largest of the row's four
+      // k-th keys cannot reach the row's top k (k keys of the row already
+      // beat it), so only the few entries above that threshold are inserted.
+      const int row = tid >> 2;
+      const int part = tid & 3;
+      const int vb0 = v0 + part * 32;
+      const float *src = &s_t[row * PK_TSTR + part * 32];
+      const uint64_t thr = graft::group_max(L.k[K - 1], 4);
+      uint32_t pass = 0;
+#pragma unroll
+      for (int j4 = 0; j4 < 32; j4 += 4) {
+        const float4 x = *reinterpret_cast<const float4 *>(src + j4);
+        const float xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = j4 + i;
+          const bool in = (vb0 + j < V) & (graft::rank_key(xs[i], vb0 + j) > thr);
+          pass |= static_cast<uint32_t>(in) << j;
+        }
+      }
+      while (pass != 0) {  // entries re-read from LDS: no dynamic register indexing
+        const int j = __builtin_ctz(pass);
+        pass &= pass - 1;
+        L.insert(graft::rank_key(src[j], vb0 + j));
+      }
+    } else {
+      // coalesced rows: 32 float4 per row
+      const bool vec = (V & 3) == 0;
+      for (int e = tid; e < BM * (PK_BV / 4); e += kThreads) {
+        const int row = e / (PK_BV / 4);
+        const int c4 = (e - row * (PK_BV / 4)) * 4;
+        const int m = m0 + row;
+        const int v = v0 + c4;
+        if (m >= M || v >= V) continue;
+        const float *src = &s_t[row * PK_TSTR + c4];
+        float *dst = logits + static_cast<size_t>(m) * V + v;
+        if (vec) {
+          *reinterpret_cast<float4 *>(dst) = make_float4(src[0], src[1], src[2], src[3]);
+        } else {
+          for (int i = 0; i < 4 && v + i < V; ++i) dst[i] = src[i];
+        }
+      }
+    }
+  }
+  if constexpr (FUSED) {
+    // k best keys of each row over this workgroup's tiles (0 = no entry)
+    const int row = tid >> 2;
+    const int part = tid & 3;
+    const int m = m0 + row;
+    for (int j = 0; j < k; ++j) {
+      const uint64_t best = graft::group_max(L.k[0], 4);
+      if (L.k[0] == best) L.pop_front();
+      if (part == 0 && m < M) part_out[(static_cast<size_t>(m) * S + map.stream) * k + j] = best;
+    }
+  }
+}
+
 }  // namespace
 
 namespace graft {
@@ -224,33 +457,103 @@ size_t lmhead_fused_ws_bytes(int M, int V, int k) {
 }
 }  // namespace graft
 
+namespace {
+int packed_tiles_m(int M) { return (M + BM - 1) / BM; }
+size_t packed_fused_ws_bytes(int M, int k) {
+  const int T = packed_tiles_m(M);
+  if (T > PK_GRID) return 0;
+  return static_cast<size_t>(M) * pk_map(0, T).streams * k * sizeof(uint64_t);
+}
+}  // namespace
+
+extern "C" size_t graft_lmhead_pack_bytes(int V, int H) {
+  if (V <= 0 || H <= 0 || H % PK_KC != 0) return 0;
+  return static_cast<size_t>((V + PK_BV - 1) / PK_BV) * PK_BV * H * 2;
+}
+
+extern "C" int graft_lmhead_pack(int V, int H, const graft_bf16 *w, graft_bf16 *w_packed, graft_stream stream) {
+  using graft::fail;
+  if (V <= 0 || H <= 0 || H % PK_KC != 0)
+    return fail(GRAFT_EINVAL, "lmhead_pack: V=%d H=%d (H must be a positive multiple of %d)", V, H, PK_KC);
+  if (!w || !w_packed) return fail(GRAFT_EINVAL, "lmhead_pack: NULL array");
+  graft::clear_error();
+  const size_t pieces = graft_lmhead_pack_bytes(V, H) / 16;
+  const size_t blocks = (pieces + 255) / 256;
+  if (blocks > 0x7FFFFFFFull) return fail(GRAFT_EINVAL, "lmhead_pack: too large");
+  hipLaunchKernelGGL(lmhead_pack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, graft::as_stream(stream), H, V,
+                     w, reinterpret_cast<u32x4 *>(w_packed), pieces);
+  return graft::check_launch("lmhead_pack");
+}
+
 extern "C" size_t graft_lmhead_topk_workspace_bytes(int M, int V, int k) {
   if (M <= 0 || V <= 0 || k <= 0) return 0;
-  const size_t a = graft::topk_plan(M, V, k).ws_bytes;
+  size_t a = graft::topk_plan(M, V, k).ws_bytes;
   const size_t b = graft::lmhead_fused_ws_bytes(M, V, k);
-  return a > b ? a : b;
+  const size_t c = packed_fused_ws_bytes(M, k);
+  if (b > a) a = b;
+  return c > a ? c : a;
 }
 
 extern "C" int graft_lmhead_topk(int M, int H, int V, int k, const graft_bf16 *hidden, const graft_bf16 *w,
-                                 float *logits, int32_t *topk_id, float *topk_val, void *ws,
+                                 int w_layout, float *logits, int32_t *topk_id, float *topk_val, void *ws,
                                  size_t ws_bytes, graft_stream stream) {
   using graft::fail;
   if (M < 0 || V <= 0 || k < 0 || k > GRAFT_MAX_K || k > V)
     return fail(GRAFT_EINVAL, "lmhead_topk: M=%d V=%d k=%d", M, V, k);
-  if (hidden && (H <= 0 || H % 64 != 0))
-    return fail(GRAFT_EINVAL, "lmhead_topk: H=%d must be a positive multiple of 64", H);
+  if (w_layout != GRAFT_W_ROWMAJOR && w_layout != GRAFT_W_PACKED)
+    return fail(GRAFT_EINVAL, "lmhead_topk: unknown weight layout %d", w_layout);
+  const bool packed = w_layout == GRAFT_W_PACKED;
+  if (hidden && (H <= 0 || H % (packed ? PK_KC : 64) != 0))
+    return fail(GRAFT_EINVAL, "lmhead_topk: H=%d must be a positive multiple of %d", H, packed ? PK_KC : 64);
   if (!hidden && !logits) return fail(GRAFT_EINVAL, "lmhead_topk: both hidden and logits are NULL");
   if (hidden && !w) return fail(GRAFT_EINVAL, "lmhead_topk: W is NULL");
   if (!logits && k == 0) return fail(GRAFT_EINVAL, "lmhead_topk: fused mode needs k > 0");
   if (!hidden && k == 0) return fail(GRAFT_EINVAL, "lmhead_topk: nothing to do (no hidden, k = 0)");
   if (k > 0 && !topk_id) return fail(GRAFT_EINVAL, "lmhead_topk: topk_id is NULL");
+  if (hidden && packed && packed_tiles_m(M) > PK_GRID)
+    return fail(GRAFT_EINVAL, "lmhead_topk: M=%d exceeds the packed path's %d rows", M, PK_GRID * BM);
+  if (hidden && packed && static_cast<size_t>(M) * H * 2 > 0xFFFFFFFFull)
+    return fail(GRAFT_EINVAL, "lmhead_topk: hidden of %d x %d exceeds 4 GiB (32-bit DMA offsets)", M, H);
   if (M == 0) return GRAFT_OK;
   const bool fused = hidden && !logits;
-  const size_t need = fused ? graft::lmhead_fused_ws_bytes(M, V, k) : (k > 0 ? graft::topk_plan(M, V, k).ws_bytes : 0);
+  size_t need = k > 0 && !fused ? graft::topk_plan(M, V, k).ws_bytes : 0;
+  if (fused) need = packed ? packed_fused_ws_bytes(M, k) : graft::lmhead_fused_ws_bytes(M, V, k);
   if (ws_bytes < need || (need > 0 && !ws))
     return fail(GRAFT_EINVAL, "lmhead_topk: workspace %zu bytes < %zu", ws_bytes, need);
   graft::clear_error();
   hipStream_t s = graft::as_stream(stream);
+  using I64 = std::integral_constant<int, 64>;
+  using I128 = std::integral_constant<int, 128>;
+  using I8 = std::integral_constant<int, 8>;
+  using I16 = std::integral_constant<int, 16>;
+  using T = std::true_type;
+  using Fz = std::false_type;
+
+  if (hidden && packed) {
+    const int tiles_m = packed_tiles_m(M);
+    const int tiles_v = (V + PK_BV - 1) / PK_BV;
+    const unsigned char *wpk = reinterpret_cast<const unsigned char *>(w);
+    auto launch = [&](auto fused_tag, auto k_tag, uint64_t *pk) {
+      constexpr bool F = decltype(fused_tag)::value;
+      constexpr int Kv = decltype(k_tag)::value;
+      hipLaunchKernelGGL((lmhead_packed_kernel<F, Kv>), dim3(PK_GRID), dim3(kThreads), 0, s, M, H, V, F ? k : 0,
+                         hidden, wpk, F ? nullptr : logits, pk, tiles_m, tiles_v);
+    };
+    if (fused) {
+      uint64_t *pk = static_cast<uint64_t *>(ws);
+      if (k <= 8) launch(T{}, I8{}, pk);
+      else launch(T{}, I16{}, pk);
+      int rc = graft::check_launch("lmhead (packed, fused top-k)");
+      if (rc != GRAFT_OK) return rc;
+      return graft::launch_topk_merge(M, pk_map(0, tiles_m).streams, k, pk, topk_id, topk_val, s);
+    }
+    launch(Fz{}, I8{}, nullptr);
+    int rc = graft::check_launch("lmhead (packed)");
+    if (rc != GRAFT_OK) return rc;
+    if (k > 0) return graft::launch_topk(M, V, k, logits, topk_id, topk_val, ws, s);
+    return GRAFT_OK;
+  }
+
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_v = (V + kBV - 1) / kBV;
   const int grid = (tiles_m * tiles_v + 7) / 8 * 8;
@@ -263,12 +566,6 @@ extern "C" int graft_lmhead_topk(int M, int H, int V, int k, const graft_bf16 *h
     hipLaunchKernelGGL((lmhead_kernel<KCv, F, Kv>), dim3(grid), dim3(kThreads), 0, s, M, H, V, F ? k : 0, hidden, w,
                        F ? nullptr : logits, pk, tiles_m, tiles_v);
   };
-  using I64 = std::integral_constant<int, 64>;
-  using I128 = std::integral_constant<int, 128>;
-  using I8 = std::integral_constant<int, 8>;
-  using I16 = std::integral_constant<int, 16>;
-  using T = std::true_type;
-  using Fz = std::false_type;
   if (fused) {
     uint64_t *pk = static_cast<uint64_t *>(ws);
     if (kc128 && k <= 8) launch(I128{}, T{}, I8{}, pk);

@@ -23,7 +23,7 @@ import numpy as np
 import torch
 
 from . import api
-from ._native import TREE_PRUNE, TREE_STATIC_REPLACE
+from ._native import TREE_PRUNE, TREE_STATIC_REPLACE, W_PACKED, W_ROWMAJOR
 
 STEPS_FUSED = ("update_retrieve", "build_tree", "tree_attention", "lmhead_topk", "accept")
 STEPS_SPLIT = ("update_retrieve", "build_tree", "tree_attention", "lmhead", "topk", "accept")
@@ -39,7 +39,11 @@ def _bf16(bits, dev):
 
 
 class VerifyRound:
-    def __init__(self, ri, w_bits=None, device="cuda", dmax: int = 8, fused: bool = True):
+    def __init__(self, ri, w_bits=None, device="cuda", dmax: int = 8, fused: bool = True,
+                 packed: bool = True):
+        """fused: lm-head and top-k in one pass (logits never stored);
+        packed: the lm-head weight is packed once here (when H % 128 == 0)
+        and the fused pass reads the packed copy."""
         dev = torch.device(device)
         self.fused = fused
         self.steps = STEPS_FUSED if fused else STEPS_SPLIT
@@ -101,6 +105,11 @@ class VerifyRound:
         self.attn_ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
 
         self.w = _bf16(w_bits, dev) if w_bits is not None else None
+        self.w_packed = None
+        if self.w is not None and packed and wl.H % 128 == 0:
+            nb = api.graft_lmhead_pack_bytes(V, wl.H)
+            self.w_packed = torch.empty(nb // 2, dtype=torch.bfloat16, device=dev)
+            api.graft_lmhead_pack(V, wl.H, self.w, self.w_packed)
         self.hidden = None
         self.logits = None if fused else torch.empty(rows, V, dtype=torch.float32, device=dev)
         self.topk_id = z(rows, k)
@@ -147,8 +156,12 @@ class VerifyRound:
         api.graft_lmhead_topk(self.rows, self.wl.H, self.V, 0, self.hidden, self.w, self.logits)
 
     def step_lmhead_topk(self):
-        api.graft_lmhead_topk(self.rows, self.wl.H, self.V, self.k, self.hidden, self.w, None,
-                              self.topk_id, self.topk_val, self.topk_ws)
+        if self.w_packed is not None:
+            api.graft_lmhead_topk(self.rows, self.wl.H, self.V, self.k, self.hidden, self.w_packed, None,
+                                  self.topk_id, self.topk_val, self.topk_ws, w_layout=W_PACKED)
+        else:
+            api.graft_lmhead_topk(self.rows, self.wl.H, self.V, self.k, self.hidden, self.w, None,
+                                  self.topk_id, self.topk_val, self.topk_ws, w_layout=W_ROWMAJOR)
 
     def step_topk(self):
         api.graft_lmhead_topk(self.rows, self.wl.H, self.V, self.k, None, None, self.logits,

@@ -11,6 +11,7 @@
  *                                depth / positions / ancestor mask
  *   graft_tree_attention         tree-masked GQA attention over the KV cache
  *   graft_lmhead_topk            logits = hidden . W^T and per-row top-k
+ *                                (weights packed once by graft_lmhead_pack)
  *   graft_accept                 deepest greedily accepted path + bonus token
  *
  * Conventions shared by every entry point
@@ -196,20 +197,42 @@ int graft_tree_attention(int B, int Hq, int Hkv, int d, float scale,
  *   logits[m, v] = sum_h hidden[m, h] * W[v, h]     (fp32 accumulate)
  *   topk_id[m, :] = the k ids of row m by (logit desc, id asc), topk_val
  *   the matching logits; argmax = topk_id[m, 0].
- * hidden (device bf16 [M, H]), w (device bf16 [V, H] row-major),
+ * hidden (device bf16 [M, H]); w (device) holds W in layout w_layout:
+ *   GRAFT_W_ROWMAJOR  bf16 [V, H] row-major, H % 64 == 0;
+ *   GRAFT_W_PACKED    the output of graft_lmhead_pack, H % 128 == 0,
+ *                     M <= 16384 (the faster path: linear weight reads).
  * logits (device fp32 [M, V]), topk_id (device int32 [M, k]),
  * topk_val (device fp32 [M, k], may be NULL).
  * Modes:  hidden && logits && k == 0      -> logits only
  *         !hidden && logits && k > 0      -> top-k of the given logits
  *         hidden && logits && k > 0       -> both, logits materialised
- * H % 64 == 0; 1 <= k <= min(GRAFT_MAX_K, V).
- * ws (device): graft_lmhead_topk_workspace_bytes(M, V, k) bytes.
+ *         hidden && !logits && k > 0      -> fused: per-row top-k of the
+ *                                            logits, which never reach
+ *                                            memory (the serving mode)
+ * The logits, and so the top-k, are bit-identical for both layouts and
+ * all modes.  1 <= k <= min(GRAFT_MAX_K, V) when k is used.
+ * ws (device): graft_lmhead_topk_workspace_bytes(M, V, k) bytes (enough
+ * for every mode and layout).
  */
+#define GRAFT_W_ROWMAJOR 0
+#define GRAFT_W_PACKED 1
 size_t graft_lmhead_topk_workspace_bytes(int M, int V, int k);
 int graft_lmhead_topk(int M, int H, int V, int k,
-                      const graft_bf16 *hidden, const graft_bf16 *w, float *logits,
+                      const graft_bf16 *hidden, const graft_bf16 *w, int w_layout, float *logits,
                       int32_t *topk_id, float *topk_val, void *ws, size_t ws_bytes,
                       graft_stream stream);
+
+/*
+ * Weight packing for graft_lmhead_topk (done once, when the lm-head is
+ * loaded; not part of a round).  w (device bf16 [V, H] row-major) is
+ * rewritten into w_packed (device, graft_lmhead_pack_bytes(V, H) bytes,
+ * caller-owned): images of 128 vocabulary rows x 128 hidden columns in
+ * tile-major, chunk-minor order, each row's 16-byte pieces XOR-swizzled
+ * by (row % 16), rows past V zero.  H % 128 == 0; returns 0 bytes /
+ * GRAFT_EINVAL otherwise.
+ */
+size_t graft_lmhead_pack_bytes(int V, int H);
+int graft_lmhead_pack(int V, int H, const graft_bf16 *w, graft_bf16 *w_packed, graft_stream stream);
 
 /*
  * Greedy acceptance (Graft page, section 2, third step: draft and

@@ -72,12 +72,18 @@ def test_host_argument_validation_launches_nothing(native):
     L = native.lib()
     E, U = native.GRAFT_EINVAL, native.GRAFT_EUNSUPPORTED
     # lm-head / top-k
-    assert L.graft_lmhead_topk(4, 256, 100, 17, 1, 1, 1, 1, None, 1, 1 << 20, None) == E
-    assert L.graft_lmhead_topk(4, 100, 100, 4, 1, 1, 1, 1, None, 1, 1 << 20, None) == E
-    assert L.graft_lmhead_topk(4, 256, 100, 0, 1, 1, None, None, None, None, 0, None) == E
-    assert L.graft_lmhead_topk(4, 256, 100, 4, None, None, None, 1, None, 1, 1 << 20, None) == E
-    assert L.graft_lmhead_topk(4, 256, 100, 200, None, None, 1, 1, None, 1, 1 << 20, None) == E
-    assert L.graft_lmhead_topk(0, 256, 100, 4, None, None, 1, 1, None, None, 0, None) == 0
+    assert L.graft_lmhead_topk(4, 256, 100, 17, 1, 1, 0, 1, 1, None, 1, 1 << 20, None) == E
+    assert L.graft_lmhead_topk(4, 100, 100, 4, 1, 1, 0, 1, 1, None, 1, 1 << 20, None) == E
+    assert L.graft_lmhead_topk(4, 256, 100, 0, 1, 1, 0, None, None, None, None, 0, None) == E
+    assert L.graft_lmhead_topk(4, 256, 100, 4, None, None, 0, None, 1, None, 1, 1 << 20, None) == E
+    assert L.graft_lmhead_topk(4, 256, 100, 200, None, None, 0, 1, 1, None, 1, 1 << 20, None) == E
+    assert L.graft_lmhead_topk(0, 256, 100, 4, None, None, 0, 1, 1, None, None, 0, None) == 0
+    # unknown weight layout; packed weights need H % 128 == 0
+    assert L.graft_lmhead_topk(4, 256, 100, 4, 1, 1, 7, None, 1, None, 1, 1 << 20, None) == E
+    assert L.graft_lmhead_topk(4, 192, 100, 4, 1, 1, 1, None, 1, None, 1, 1 << 20, None) == E
+    assert L.graft_lmhead_topk(17000, 256, 100, 4, 1, 1, 1, None, 1, None, 1, 1 << 30, None) == E
+    assert L.graft_lmhead_pack(100, 192, 1, 1, None) == E
+    assert L.graft_lmhead_pack(100, 256, None, 1, None) == E
     # attention
     args = [1, 1, 1, 1, 1 << 20, 1, 100, 1, 10, 1, 1, 1, None, None, 0, None, None]
     assert L.graft_tree_attention(1, 8, 2, 96, 0.1, *args) == U
@@ -103,6 +109,13 @@ def test_host_argument_validation_launches_nothing(native):
 
 def test_workspace_sizes(native):
     L = native.lib()
+    # packed weights: whole 128-row tiles, rows past V padded
+    assert L.graft_lmhead_pack_bytes(100, 256) == 128 * 256 * 2
+    assert L.graft_lmhead_pack_bytes(128256, 4096) == 128256 * 4096 * 2
+    assert L.graft_lmhead_pack_bytes(129, 128) == 256 * 128 * 2
+    assert L.graft_lmhead_pack_bytes(100, 192) == 0
+    # one key list per (row, persistent workgroup) fits in the advertised workspace
+    assert L.graft_lmhead_topk_workspace_bytes(60, 1000, 8) >= 60 * 256 * 8 * 8
     assert L.graft_lmhead_topk_workspace_bytes(60, 128256, 8) > 0
     assert L.graft_lmhead_topk_workspace_bytes(0, 128256, 8) == 0
     # tiny single-split attention needs no workspace; long context does

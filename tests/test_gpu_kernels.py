@@ -130,6 +130,84 @@ def test_fused_lmhead_topk_equals_split(api, M, H, V, k):
     assert np.array_equal(vals.cpu().numpy(), ev)
 
 
+# ----------------------------------------------------------------------------- packed lm-head
+
+def _pack_np(w, V, H):
+    """The packed layout as include/graft.h states it: images of 128 rows x
+    128 columns, tile-major then chunk; slot s of row r holds 16-byte piece
+    s ^ (r % 16); rows past V are zero."""
+    T, nch = (V + 127) // 128, H // 128
+    wp = np.zeros((T * 128, H), np.uint16)
+    wp[:V] = w
+    x = wp.reshape(T, 128, nch, 16, 8).transpose(0, 2, 1, 3, 4)  # [T][c][r][piece][8]
+    r = np.arange(128)[:, None]
+    src = np.arange(16)[None, :] ^ (r % 16)
+    return x[:, :, r, src, :].reshape(-1)
+
+
+def _packed(api, w, V, H):
+    wd = dev_bf16(w)
+    wp = torch.empty(api.graft_lmhead_pack_bytes(V, H) // 2, dtype=torch.bfloat16, device="cuda")
+    api.graft_lmhead_pack(V, H, wd, wp)
+    return wd, wp
+
+
+@pytest.mark.parametrize("V,H", [(100, 256), (1001, 384), (128, 128)])
+def test_lmhead_pack_layout(api, V, H):
+    r = np.random.default_rng(V + H)
+    w = r.integers(0, 1 << 16, (V, H), dtype=np.uint16)
+    w[(w & 0x7F80) == 0x7F80] = 0  # no NaN/Inf bit patterns
+    _, wp = _packed(api, w, V, H)
+    torch.cuda.synchronize()
+    got = wp.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, _pack_np(w, V, H))
+
+
+@pytest.mark.parametrize("M,H,V", [(1, 128, 129), (15, 256, 1024), (65, 384, 1001), (130, 512, 777),
+                                   (60, 4096, 3000), (2112, 128, 300)])
+def test_lmhead_packed_equals_rowmajor(api, M, H, V):
+    """Both layouts run the same MFMA sequence: identical logits, bit for bit
+    (m tiles 1, 2, 3, 33 cover both workgroup mappings)."""
+    say(f"[lmhead packed] M={M} H={H} V={V}")
+    r = np.random.default_rng(M * 5 + H + V)
+    h = f32_to_bf16_bits(r.standard_normal((M, H)).astype(np.float32))
+    w = f32_to_bf16_bits((0.02 * r.standard_normal((V, H))).astype(np.float32))
+    hd = dev_bf16(h)
+    wd, wp = _packed(api, w, V, H)
+    a = torch.empty(M, V, dtype=torch.float32, device="cuda")
+    b = torch.empty(M, V, dtype=torch.float32, device="cuda")
+    api.graft_lmhead_topk(M, H, V, 0, hd, wd, a)
+    api.graft_lmhead_topk(M, H, V, 0, hd, wp, b, w_layout=1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    rows = np.unique(np.linspace(0, M - 1, min(M, 8)).astype(int))
+    ok, e = within_tol(b.cpu().numpy()[rows].astype(np.float64), OL.logits(h[rows], w).astype(np.float64))
+    assert ok, e
+
+
+@pytest.mark.parametrize("M,H,V,k", [(60, 4096, 128256, 8), (130, 384, 1001, 16), (1, 128, 5, 3),
+                                     (64, 256, 129, 10), (300, 128, 2000, 16), (2112, 128, 300, 8)])
+def test_fused_packed_topk_equals_split(api, M, H, V, k):
+    """Packed fused top-k (lists kept per workgroup across tiles) ranks
+    exactly the logits the split row-major mode writes."""
+    say(f"[fused packed lmhead+topk] M={M} H={H} V={V} k={k}")
+    r = np.random.default_rng(M * 11 + V)
+    h = f32_to_bf16_bits(r.standard_normal((M, H)).astype(np.float32))
+    w = f32_to_bf16_bits((0.02 * r.standard_normal((V, H))).astype(np.float32))
+    hd = dev_bf16(h)
+    wd, wp = _packed(api, w, V, H)
+    logits = torch.empty(M, V, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(api.graft_lmhead_topk_workspace_bytes(M, V, k), 1), dtype=torch.uint8, device="cuda")
+    api.graft_lmhead_topk(M, H, V, 0, hd, wd, logits)
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    vals = torch.empty(M, k, dtype=torch.float32, device="cuda")
+    api.graft_lmhead_topk(M, H, V, k, hd, wp, None, ids, vals, ws, w_layout=1)
+    torch.cuda.synchronize()
+    eid, ev = OT.topk(logits.cpu().numpy(), k)
+    assert np.array_equal(ids.cpu().numpy(), eid)
+    assert np.array_equal(vals.cpu().numpy(), ev)
+
+
 # ----------------------------------------------------------------------------- accept
 
 def _accept_gpu(api, n, row_off, parent, token, argmax):
