@@ -7,16 +7,24 @@
 // iff bit j of mask[i].  All N tree nodes times the G = Hq/Hkv heads of one
 // KV head share every K/V tile, so one workgroup owns one (request, KV head,
 // key split) and all of its N*G query rows: K/V are read from HBM once per
-// split and staged through LDS, and both products run on MFMA:
+// split, and both products run on MFMA:
 //   S^T = K . Q^T   (A = K tile from LDS, B = Q fragments kept in registers)
-//   O^T = V^T . P^T (A = V^T tile from LDS, B = P straight from the S^T
+//   O^T = V^T . P^T (A = V^T fragments from LDS, B = P straight from the S^T
 //                    accumulators, re-packed to bf16)
 // Computing the transposes puts one query row per lane column in both
 // accumulators, so the online-softmax statistics of a row live in one lane
 // group and rescaling O needs no cross-lane traffic.  A V_MFMA_F32_16X16X32
 // lane holds keys {4g..4g+3} and {16+4g..16+4g+3} of its row after the S^T
-// step; the P^T operand uses exactly that key set, and the V^T fragment is
-// read with the same set, so no shuffle is needed between the two products.
+// step; the P^T operand uses exactly that key set, and so does the V^T
+// fragment, so no shuffle is needed between the two products.
+//
+// Staging: K and V chunks of 64 keys are copied HBM -> LDS in their cache
+// layout by LDS DMA (global_load_lds_dwordx4: no registers, no VALU) into a
+// 4-stage ring, with each key row's 16-byte pieces XOR-swizzled so that the
+// fragment reads below are free of bank conflicts.  K fragments are plain
+// 16-byte LDS reads; V^T fragments come from ds_read_b64_tr_b16, whose
+// 16-lane transpose turns 4 keys x 16 head-dim columns of V into each lane
+// holding 4 keys of one column (two reads per fragment).
 //
 // The key range is split over workgroups (8 KV heads alone cannot fill 256
 // CUs); each split writes unnormalised O, the running max and the exp-sum,
@@ -37,21 +45,71 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int KCH = 64;      // keys per staged chunk (four 16-key MFMA blocks)
-constexpr int MIN_SPLIT = 256;
+constexpr int NS = 4;        // LDS ring stages
+constexpr int MIN_SPLIT = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ inline bf16x8 zero8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
 __device__ inline u32x4 load16(const graft_bf16 *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-// Double-buffered K and V^T tiles of one KCH-key chunk.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// Geometry of one ring stage for head dim D: the K chunk then the V chunk,
+// each 64 key rows of D bf16 in cache order.  Row r keeps 16-byte piece p at
+// slot p ^ swz(r); K and V use different swizzles because they are read with
+// different lane patterns (16 consecutive rows of one piece for K; 8 rows x
+// 2 pieces per half-wave for the V transpose reads).
 template <int D>
-struct Smem {
-  static constexpr int KSTR = D + 8;    // bf16 per K row (16 B pad)
-  static constexpr int VSTR = KCH + 4;  // bf16 per V^T row (8 B pad: 16 rows of a fragment hit 32 banks)
-  graft_bf16 k[2][KCH * KSTR];
-  graft_bf16 vt[2][D * VSTR];
+struct Tile {
+  static constexpr int ROW = D * 2;            // bytes per key row
+  static constexpr int RPB = 256 / ROW;        // rows per 256-byte LDS bank line
+  static constexpr int KB = KCH * ROW;         // bytes of the K (or V) chunk
+  static constexpr int SB = 2 * KB;            // bytes per ring stage
+  static constexpr int DI = KB / 1024 / kWaves;  // DMA instructions per wave for K (and for V)
+  static_assert(DI >= 1, "each wave copies at least one KiB of K and of V");
+  __device__ static int swz_k(int r) { return (r / RPB) & (D / 8 - 1); }
+  __device__ static int swz_v(int r) { return 2 * ((r / RPB) & (D / 16 - 1)); }
 };
+
+// 16-byte LDS DMA (lane l's bytes from sbase + voff land at LDS byte lds +
+// 16 l), issued through asm so that the compiler does not serialise the ring
+// with conservative waits; completion is tracked by hand with vmcnt.
+__device__ inline void lds_dma16(unsigned lds, const void *sbase, unsigned voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+// Max / sum over the 4 lanes l16, l16+16, l16+32, l16+48 (the lane groups
+// that hold one query row), with the gfx950 row-swap permutes: VALU only,
+// no LDS traffic.
+__device__ inline float group4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float group4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// A wave-uniform pointer the compiler may keep in registers loaded per lane
+// (a vector load of kv_off), moved to scalar registers for the DMA base.
+__device__ inline const unsigned char *uniform_ptr(const unsigned char *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const unsigned char *>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+// Wait until at most N of this wave's DMAs are outstanding and its LDS
+// accesses have completed, then meet the other waves.
+template <int N>
+__device__ inline void ring_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 struct Params {
   int B, Hq, Hkv, G;
@@ -75,33 +133,32 @@ struct Params {
   int32_t *err;
 };
 
+// Per-request scalars read through the constant address space: scalar
+// loads, which the compiler does not count against the vector-memory
+// counter that tracks the DMA ring (the arrays are not written here).
+template <typename T>
+__device__ inline T ld_scalar(const T *p) {
+  return *(const __attribute__((address_space(4))) T *)p;
+}
+
 // Returns false (and flags once) when the request's lengths exceed the
 // bounds the grid was sized for or its row capacity.
 __device__ inline bool request_ok(const Params &P, int b, int &ctx, int &n) {
-  ctx = P.ctx_len[b];
-  n = P.n[b];
+  ctx = ld_scalar(P.ctx_len + b);
+  n = ld_scalar(P.n + b);
   const bool ok = ctx >= 0 && ctx <= P.max_ctx && n >= 1 && n <= P.max_n && n <= GRAFT_MAX_NODES &&
-                  n <= P.row_off[b + 1] - P.row_off[b];
+                  n <= ld_scalar(P.row_off + b + 1) - ld_scalar(P.row_off + b);
   if (!ok && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) graft::raise_flag(P.err, GRAFT_ERR_CAPACITY);
   return ok;
 }
 
-// Registers of one chunk in flight: KP 16-byte K pieces and (for threads that
-// stage V) the same 8 head-dim columns of two consecutive keys.
-template <int D>
-struct Stage {
-  static constexpr int KP = KCH * D / 8 / kThreads;  // K pieces per thread
-  u32x4 k[KP];
-  u32x4 va, vb;
-};
-
 template <int D, int RBW>
-__global__ __launch_bounds__(kThreads, RBW == 1 ? 2 : 1) void tree_attn_kernel(Params P) {
+__global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
+  using TL = Tile<D>;
   constexpr int DS = D / 32;  // MFMA k-steps over the head dim
   constexpr int DB = D / 16;  // 16-wide output blocks over the head dim
-  constexpr int KP = Stage<D>::KP;
-  constexpr int VTHREADS = (KCH / 2) * (D / 8);  // threads staging a V key pair
-  __shared__ __attribute__((aligned(16))) Smem<D> sm;
+  constexpr int DI = TL::DI;
+  __shared__ __attribute__((aligned(1024))) unsigned char sm[NS * TL::SB];
 
   const int b = blockIdx.z;
   const int h = blockIdx.y / P.row_groups;
@@ -119,13 +176,50 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? 2 : 1) void tree_attn_kernel(P
   const int nch = (k_end - k_begin + KCH - 1) / KCH;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int g = lane >> 4;
-  const int r_off = P.row_off[b];
+  const int r_off = ld_scalar(P.row_off + b);
 
-  // ---- this lane's query rows: Q fragments and tree-mask words
+  // ---- LDS DMA ring.  Lane l of this wave's i-th K (V) instruction copies
+  // piece (slot ^ swz(row)) of key row `row` of the chunk into slot `slot`.
+  // Slots past k_end re-read the last valid slot (in bounds; their scores
+  // are masked and their P is 0).
+  const unsigned sbase = static_cast<unsigned>(reinterpret_cast<size_t>((lds_u8 *)sm));
+  const size_t kv_base = static_cast<size_t>(ld_scalar(P.kv_off + b)) + static_cast<size_t>(h) * P.head_stride;
+  const unsigned char *kbase = uniform_ptr(reinterpret_cast<const unsigned char *>(P.kc + kv_base));
+  const unsigned char *vbase = uniform_ptr(reinterpret_cast<const unsigned char *>(P.vc + kv_base));
+  int drow[DI];
+  unsigned kpc[DI], vpc[DI];
+#pragma unroll
+  for (int i = 0; i < DI; ++i) {
+    const int byte = (wave * DI + i) * 1024 + lane * 16;
+    const int r = byte / TL::ROW;
+    const int slot = (byte - r * TL::ROW) / 16;
+    drow[i] = r;
+    kpc[i] = ((slot ^ TL::swz_k(r)) * 16);
+    vpc[i] = ((slot ^ TL::swz_v(r)) * 16);
+  }
+  auto issue = [&](int c) {
+    const int c0 = k_begin + c * KCH;
+    const unsigned kl = sbase + (c % NS) * TL::SB + wave * DI * 1024;
+#pragma unroll
+    for (int i = 0; i < DI; ++i) {
+      const unsigned srow = static_cast<unsigned>(min(c0 + drow[i], k_end - 1)) * TL::ROW;
+      lds_dma16(kl + i * 1024, kbase, srow + kpc[i]);
+      lds_dma16(kl + TL::KB + i * 1024, vbase, srow + vpc[i]);
+    }
+  };
+
+  // ---- ring prologue first: chunks 0 .. NS-2 go in flight before anything
+  // else is loaded
+#pragma unroll
+  for (int c = 0; c < NS - 1; ++c)
+    if (c < nch) issue(c);
+
+  // ---- this lane's query rows: Q fragments and tree-mask words (their
+  // latency overlaps the first chunks')
   bf16x8 qf[RBW][DS];
   uint64_t mrow[RBW];
   bool rvalid[RBW];
@@ -156,182 +250,134 @@ __global__ __launch_bounds__(kThreads, RBW == 1 ? 2 : 1) void tree_attn_kernel(P
     for (int db = 0; db < DB; ++db) oacc[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- staging.  Loads are unconditional: slots past k_end read the last
-  // valid slot (their scores are masked and their P is 0), which keeps the
-  // compiler from draining the memory pipeline at branch joins.
-  const size_t kv_base = static_cast<size_t>(P.kv_off[b]) + static_cast<size_t>(h) * P.head_stride;
-  // every thread stages V at d = 128; at d = 64 waves 0-3 do (wave-uniform)
-  const bool vstager = VTHREADS >= kThreads || __builtin_amdgcn_readfirstlane(tid < VTHREADS ? 1 : 0) != 0;
-  const int vcol = tid % (D / 8);
-  const int vkp = tid / (D / 8);  // key pair
-  auto fetch = [&](Stage<D> &st, int c) {
+  // per-lane fragment offsets (the swizzles depend only on the lane)
+  const int swk = TL::swz_k(l16);                  // K rows 32t + 16kb + l16
+  const int vr = 4 * g + (l16 >> 2);               // V rows 32t + vr (+16)
+  const int swv = TL::swz_v(vr);
+  const int vcol = 4 * (l16 & 3);                  // first head-dim column within the 16-block
+  const int kfrag = l16 * TL::ROW;
+  const int vfrag = vr * TL::ROW + 8 * ((vcol >> 2) & 1);
+
+  // One chunk: S^T for its 64 keys, one online-softmax update per row
+  // block, then O^T += V^T . P^T over its two 32-key halves.
+  auto compute = [&](int c) {
+    const lds_u8 *ks = (const lds_u8 *)sm + (c % NS) * TL::SB;
+    const lds_u8 *vs = ks + TL::KB;
     const int c0 = k_begin + c * KCH;
+    // S^T blocks: sacc[j][kb][i] = S[row l16][key c0 + kb*16 + 4g + i]
+    f32x4 sacc[RBW][4];
 #pragma unroll
-    for (int j = 0; j < KP; ++j) {
-      const int p = tid + j * kThreads;
-      const int key = p / (D / 8);
-      const int col = p - key * (D / 8);
-      const int slot = min(c0 + key, k_end - 1);
-      st.k[j] = load16(P.kc + kv_base + static_cast<size_t>(slot) * D + col * 8);
-    }
-    if (vstager) {
-      const int s0 = min(c0 + 2 * vkp, k_end - 1);
-      const int s1 = min(c0 + 2 * vkp + 1, k_end - 1);
-      st.va = load16(P.vc + kv_base + static_cast<size_t>(s0) * D + vcol * 8);
-      st.vb = load16(P.vc + kv_base + static_cast<size_t>(s1) * D + vcol * 8);
-    }
-  };
-  auto store = [&](const Stage<D> &st, int buf) {
+    for (int j = 0; j < RBW; ++j)
 #pragma unroll
-    for (int j = 0; j < KP; ++j) {
-      const int p = tid + j * kThreads;
-      const int key = p / (D / 8);
-      const int col = p - key * (D / 8);
-      *reinterpret_cast<u32x4 *>(&sm.k[buf][key * Smem<D>::KSTR + col * 8]) = st.k[j];
-    }
-    if (vstager) {
-      // V^T[d][2kp], V^T[d][2kp+1] packed into one 32-bit word per head dim
+      for (int kb = 0; kb < 4; ++kb) sacc[j][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t a = st.va[e >> 1], bw = st.vb[e >> 1];
-        const uint32_t word = (e & 1) ? ((a >> 16) | (bw & 0xFFFF0000u)) : ((a & 0xFFFFu) | (bw << 16));
-        *reinterpret_cast<uint32_t *>(&sm.vt[buf][(vcol * 8 + e) * Smem<D>::VSTR + 2 * vkp]) = word;
-      }
-    }
-  };
-  // One chunk = two 32-key halves; each half runs S^T, the online-softmax
-  // update and O^T += V^T . P^T, so only two S^T blocks are live at a time.
-  auto compute = [&](int c, int buf) {
+    for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int c0 = k_begin + c * KCH + 32 * t;
-      // S^T blocks: sacc[j][kb][i] = S[row l16][key c0 + kb*16 + 4g + i]
-      f32x4 sacc[RBW][2];
-#pragma unroll
-      for (int j = 0; j < RBW; ++j) {
-        sacc[j][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sacc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-              &sm.k[buf][(32 * t + kb * 16 + l16) * Smem<D>::KSTR + s * 32 + 8 * g]);
-#pragma unroll
-          for (int j = 0; j < RBW; ++j)
-            if (active[j]) sacc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j][s], sacc[j][kb], 0, 0, 0);
-        }
-      }
-      // online softmax (base 2) and the P^T operand of this half.  A half
-      // that lies entirely inside the context needs no mask (uniform test).
-      const bool unmasked = c0 + 32 <= ctx && c0 + 32 <= k_end;
-      bf16x8 pb[RBW];
-#pragma unroll
-      for (int j = 0; j < RBW; ++j) {
-        if (!active[j]) continue;
-        // raw scores; the scale is folded into the exp2 argument below
-        float x[8];
-        if (unmasked) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[kb * 4 + i] = sacc[j][kb][i];
-        } else {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = c0 + kb * 16 + 4 * g + i;
-              const bool tree_vis = ((mrow[j] >> ((key - ctx) & 63)) & 1ull) != 0;
-              const bool vis = (key < k_end) & ((key < ctx) | tree_vis);  // no short-circuit branches
-              x[kb * 4 + i] = vis ? sacc[j][kb][i] : -INFINITY;
-            }
-        }
-        float cmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-        cmax *= P.scale_log2;  // scale > 0: max commutes with it
-        // Lazy rescaling: the running max m only moves when some row of the
-        // wave sees a score more than 8 (log2 units) above it, so p stays
-        // <= 2^8 and O, l keep sharing the same m (the final O / l is
-        // unchanged); most halves then skip the O rescale entirely.
-        const bool grow = cmax > m_run[j] + 8.f;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
-          // rows that do not grow keep alpha = 1 (also when m is still -inf)
-          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[j] - cmax) : 1.f;  // 0 from -inf
-          l_run[j] *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[j][db] *= alpha;
-          m_run[j] = grow ? cmax : m_run[j];
-        }
-        // rows with nothing visible yet keep m = -inf: shift by 0 (p = 0)
-        const float m_use = m_run[j] == -INFINITY ? 0.f : m_run[j];
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], P.scale_log2, -m_use));
-          psum += x[e];
-        }
-        l_run[j] += psum;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[j][e] = static_cast<__bf16>(x[e]);
-      }
-      // O^T += V^T . P^T (keys {4g..4g+3} and {16+4g..16+4g+3} of the half)
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const graft_bf16 *vrow = &sm.vt[buf][(db * 16 + l16) * Smem<D>::VSTR + 32 * t];
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow + 4 * g);
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 16 + 4 * g);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+      for (int s = 0; s < DS; ++s) {
+        const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8 *)(
+            ks + 16 * kb * TL::ROW + kfrag + (((4 * s + g) ^ swk) * 16));
 #pragma unroll
         for (int j = 0; j < RBW; ++j)
-          if (active[j]) oacc[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[j], oacc[j][db], 0, 0, 0);
+          if (active[j]) sacc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j][s], sacc[j][kb], 0, 0, 0);
+      }
+    }
+    // online softmax (base 2).  A chunk that lies entirely inside the
+    // context needs no mask (uniform test).
+    const bool unmasked = c0 + KCH <= ctx && c0 + KCH <= k_end;
+    bf16x8 pb[RBW][2];  // P^T operand of each 32-key half
+#pragma unroll
+    for (int j = 0; j < RBW; ++j) {
+      if (!active[j]) continue;
+      // raw scores; the scale is folded into the exp2 argument below
+      float x[16];
+      if (unmasked) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[kb * 4 + i] = sacc[j][kb][i];
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = c0 + kb * 16 + 4 * g + i;
+            const bool tree_vis = ((mrow[j] >> ((key - ctx) & 63)) & 1ull) != 0;
+            const bool vis = (key < k_end) & ((key < ctx) | tree_vis);  // no short-circuit branches
+            x[kb * 4 + i] = vis ? sacc[j][kb][i] : -INFINITY;
+          }
+      }
+      float cmax = x[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) cmax = fmaxf(cmax, x[e]);
+      cmax = group4_max(cmax) * P.scale_log2;  // scale > 0: max commutes with it
+      // Lazy rescaling: the running max m only moves when some row of the
+      // wave sees a score more than 8 (log2 units) above it, so p stays
+      // <= 2^8 and O, l keep sharing the same m (the final O / l is
+      // unchanged); most chunks then skip the O rescale entirely.
+      const bool grow = cmax > m_run[j] + 8.f;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform
+        // rows that do not grow keep alpha = 1 (also when m is still -inf)
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[j] - cmax) : 1.f;  // 0 from -inf
+        l_run[j] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[j][db] *= alpha;
+        m_run[j] = grow ? cmax : m_run[j];
+      }
+      // rows with nothing visible yet keep m = -inf: shift by 0 (p = 0)
+      const float m_use = m_run[j] == -INFINITY ? 0.f : m_run[j];
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], P.scale_log2, -m_use));
+        psum += x[e];
+      }
+      l_run[j] += psum;
+      // half t holds keys {32t + 4g + i} (block 2t) and {32t + 16 + 4g + i}
+      // (block 2t + 1)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[j][t][e] = static_cast<__bf16>(x[8 * t + e]);
+    }
+    // O^T += V^T . P^T: lane (d = db*16 + l16, g) needs keys {4g..4g+3}
+    // and {16+4g..16+4g+3} of the half for head-dim column d; the 16-lane
+    // transpose read delivers them when lane a of the group points at key
+    // row 4g + a/4, columns db*16 + 4(a%4) .. +3.
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int piece = 2 * db + ((vcol >> 3) & 1);
+        const lds_u8 *va = vs + 32 * t * TL::ROW + vfrag + ((piece ^ swv) * 16);
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)va);
+        const s16x4 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(va + 16 * TL::ROW));
+        const u32x2 lw = __builtin_bit_cast(u32x2, lo);
+        const u32x2 hw = __builtin_bit_cast(u32x2, hi);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], hw[0], hw[1]});
+#pragma unroll
+        for (int j = 0; j < RBW; ++j)
+          if (active[j]) oacc[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[j][t], oacc[j][db], 0, 0, 0);
       }
     }
   };
 
-  if constexpr (RBW < 3) {
-    // Two register stages in strict ping-pong and two LDS buffers: while
-    // chunk c is computed, chunks c+1 and c+2 are in flight.
-    Stage<D> A, Bst;
-    fetch(A, 0);
-    store(A, 0);
-    fetch(A, min(1, nch - 1));
-    __syncthreads();
-    for (int c = 0; c < nch; c += 2) {
-      fetch(Bst, min(c + 2, nch - 1));
-      compute(c, 0);
-      store(A, 1);
-      __syncthreads();
-      if (c + 1 >= nch) break;
-      fetch(A, min(c + 3, nch - 1));
-      compute(c + 1, 1);
-      store(Bst, 0);
-      __syncthreads();
-    }
-  } else {
-    // three row blocks per wave leave registers for one stage only: chunk c+1
-    // is in flight while chunk c is computed
-    Stage<D> A;
-    fetch(A, 0);
-    store(A, 0);
-    __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-      fetch(A, min(c + 1, nch - 1));
-      compute(c, c & 1);
-      store(A, (c + 1) & 1);
-      __syncthreads();
-    }
+  // ---- ring: chunks c+1 .. c+NS-2 stay in flight while chunk c is computed
+  constexpr int PER = 2 * DI;  // DMAs per wave per chunk
+  for (int c = 0; c < nch; ++c) {
+    const int younger = min(nch - 1 - c, NS - 2);  // chunks issued after c
+    if (younger >= 2) ring_barrier<2 * PER>();
+    else if (younger == 1) ring_barrier<PER>();
+    else ring_barrier<0>();
+    if (c + NS - 1 < nch) issue(c + NS - 1);  // into the stage chunk c - 1 used
+    compute(c);
   }
 
   // ---- epilogue: oacc[j][db][i] = O[row l16][d = db*16 + 4g + i]
 #pragma unroll
   for (int j = 0; j < RBW; ++j) {
     if (!active[j]) continue;
-    float l_tot = l_run[j];
-    l_tot += __shfl_xor(l_tot, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = group4_sum(l_run[j]);
     if (!rvalid[j]) continue;
     const int r = row_lo + (wave * RBW + j) * 16 + l16;
     if (P.nsplit == 1) {
@@ -423,23 +469,22 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int max_n) {
   const int rows = max_n * G;
   const int rb = (rows + 15) / 16;
   const long long L = static_cast<long long>(max_ctx) + max_n;
-  const long long min_splits = (L + MIN_SPLIT - 1) / MIN_SPLIT;
-  // fewest row groups that fit (at most 3 row blocks per wave: 4 spill at
-  // d = 128), unless even the finest key split leaves the chip half idle --
-  // then one row block per wave (two resident workgroups per CU, more groups)
+  // fewest row groups that fit (at most 3 row blocks per wave): every group
+  // re-reads the K/V tiles from LDS once per wave, so more rows per wave
+  // means less LDS traffic per query row
   if (rb <= kWaves) p.rbw = 1;
   else if (rb <= 2 * kWaves) p.rbw = 2;
   else p.rbw = 3;
-  if (p.rbw > 1 && static_cast<long long>(B) * Hkv * ((rb + kWaves * p.rbw - 1) / (kWaves * p.rbw)) * min_splits < 256)
-    p.rbw = 1;
   p.rows_per_wg = kWaves * p.rbw * 16;
   p.row_groups = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
   p.rows_cap = rb * 16;
+  // one workgroup per CU (the LDS ring takes most of a CU's LDS): split the
+  // keys so that about 256 workgroups run at once
   const long long units = static_cast<long long>(B) * Hkv * p.row_groups;
-  long long want = units > 0 ? (384 + units - 1) / units : 1;
+  long long want = units > 0 ? (256 + units - 1) / units : 1;
   if (want < 1) want = 1;
   long long len = (L + want - 1) / want;
-  len = (len + KCH - 1) / KCH * KCH;
+  len = (len + 31) / 32 * 32;
   if (len < MIN_SPLIT) len = MIN_SPLIT;
   p.split_len = static_cast<int>(len);
   p.nsplit = static_cast<int>((L + len - 1) / len);
