@@ -9,16 +9,21 @@
 // the slot count and swaps low-confidence draft nodes for table successors
 // (Graft page, section 4, batched-serving paragraph).
 //
-// One workgroup per request.  Ranking is a rank count in LDS (candidate
-// pools are a few hundred entries, so the C^2 compares are cheap once the
-// LDS reads are vectorised); the <= 64 flattened nodes map one per
-// lane of wave 0, where ancestor masks and depths come from six rounds of
-// pointer jumping over the parent links.
+// One workgroup of 512 threads per request.  Every input array is staged in
+// LDS by one round of loads.  Ranking is a rank count: one candidate per
+// thread compares its 64-bit key with every other key (broadcast LDS reads,
+// one unsigned compare per pair), and a wavefront stops as soon as each of
+// its candidates already has budget-1 better ones.  Flattened indices come
+// from a ballot / bit-count prefix scan.  The <= 64 flattened nodes map one
+// per lane of wave 0, where ancestor masks and depths come from six rounds
+// of pointer jumping over the parent links.
 #include "common.h"
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWavesBT = kThreads / 64;
+constexpr int kPasses = GRAFT_MAX_CAND / kThreads;  // candidate passes of one thread
 
 __device__ void write_padding(int from, int to, int32_t *parent, int32_t *token, int32_t *depth,
                               int32_t *pos, uint64_t *mask, int8_t *src) {
@@ -44,15 +49,21 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     int8_t *__restrict__ o_src, int32_t *__restrict__ err) {
   __shared__ float s_score[GRAFT_MAX_CAND];
   __shared__ __attribute__((aligned(16))) uint64_t s_key[GRAFT_MAX_CAND];
-  __shared__ int s_idx[GRAFT_MAX_CAND];  // kept flag, then flattened index or -1
-  __shared__ int s_part[kThreads];
+  __shared__ int s_par[GRAFT_MAX_CAND];
+  __shared__ int s_ctok[GRAFT_MAX_CAND];
+  __shared__ int s_idx[GRAFT_MAX_CAND];  // flattened index or -1
+  __shared__ int s_wtot[kPasses * kWavesBT];
   __shared__ int s_np[GRAFT_MAX_NODES];
   __shared__ int s_nt[GRAFT_MAX_NODES];
   __shared__ int s_nsrc[GRAFT_MAX_NODES];
   __shared__ int s_low[GRAFT_MAX_NODES];
+  __shared__ int s_rpar[GRAFT_MAX_NODES];
+  __shared__ int s_rtok[GRAFT_MAX_NODES];
 
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane64 = tid & 63;
   const int c0 = cand_off[b];
   const int C = cand_off[b + 1] - c0;
   const int r0 = row_off[b];
@@ -61,6 +72,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
   const int R = (mode == GRAFT_TREE_PRUNE && ret_off) ? ret_off[b + 1] - ret_off[b] : 0;
   const int ro = R > 0 ? ret_off[b] : 0;
   const int bud = budget[b];
+  const int ctx = ctx_len[b];
 
   if (C < 1 || C > max_cand || bud < 1 || R < 0) {
     if (tid == 0) {
@@ -71,62 +83,78 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     return;
   }
 
-  // Ranking key of candidate c >= 1: (order(score) << 11) | (2047 - c), so
-  // "o ranks before c" (higher score, ties to the lower index) is exactly
-  // key_o > key_c.  The root's slot and the padding hold key 0, below every
-  // real key.  Counting uses the borrow bit of key_c - key_o: pure integer
-  // VALU work, no lane masks.
+  // Stage everything in one round of loads.  Ranking key of candidate c >= 1:
+  // (order(score) << 11) | (2047 - c), so "o ranks before c" (higher score,
+  // ties to the lower index) is exactly key_o > key_c; the root's slot and
+  // the padding hold key 0, below every real key.
   const int Cp = (C + 1) & ~1;
   for (int c = tid; c < Cp; c += kThreads) {
     uint64_t key = 0;
     if (c < C) {
       const float sc = cand_score[c0 + c];
-      int p = cand_parent[c0 + c];
-      bool pok = c == 0 ? p == -1 : (p >= 0 && p < c);
+      const int p = cand_parent[c0 + c];
+      const int t = cand_token[c0 + c];
+      const bool pok = c == 0 ? p == -1 : (p >= 0 && p < c);
       if (!pok) graft::raise_flag(err, GRAFT_ERR_PARENT);
-      int t = cand_token[c0 + c];
       if (t < 0 || t >= V) graft::raise_flag(err, GRAFT_ERR_TOKEN);
       s_score[c] = sc;
+      s_par[c] = p;
+      s_ctok[c] = t;
       if (c > 0) key = (static_cast<uint64_t>(graft::float_order(sc)) << 11) | static_cast<uint64_t>(2047 - c);
     }
     s_key[c] = key;
   }
+  for (int r = tid; r < R && r < GRAFT_MAX_NODES; r += kThreads) {
+    s_rpar[r] = ret_parent[ro + r];
+    s_rtok[r] = ret_token[ro + r];
+  }
   __syncthreads();
 
-  // keep the root and every candidate with fewer than bud-1 better others
-  for (int c = tid; c < C; c += kThreads) {
-    const uint64_t kc = s_key[c];
+  // keep the root and every candidate with fewer than bud-1 better others;
+  // one candidate per thread, one 64-bit compare per (candidate, other) pair
+  // on broadcast LDS reads; a wavefront stops once each of its candidates
+  // already has bud-1 better ones
+  const uint64_t need = static_cast<uint64_t>(bud - 1);
+  const ulonglong2 *kv = reinterpret_cast<const ulonglong2 *>(s_key);
+  for (int pass = 0; pass < kPasses; ++pass) {
+    if (pass * kThreads >= C) break;  // uniform
+    const int c = pass * kThreads + tid;
+    const bool live = c < C;
+    const uint64_t kc = live ? s_key[c] : ~0ull;  // padding lanes count nothing
     uint64_t cnt = 0;
-#pragma unroll 8
-    for (int o2 = 0; o2 < Cp; o2 += 2) {
-      const ulonglong2 q = *reinterpret_cast<const ulonglong2 *>(&s_key[o2]);
-      cnt += (kc - q.x) >> 63;
-      cnt += (kc - q.y) >> 63;
+    for (int o2 = 0; o2 < Cp / 2; o2 += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const ulonglong2 q = kv[min(o2 + u, Cp / 2 - 1)];
+        const uint64_t w = o2 + u < Cp / 2 ? 1ull : 0ull;
+        cnt += (q.x > kc ? w : 0ull) + (q.y > kc ? w : 0ull);
+      }
+      // every live candidate of this wavefront already excluded (the root
+      // stays in regardless)
+      if (__builtin_amdgcn_ballot_w64(live && c > 0 && cnt < need) == 0) break;
     }
-    s_idx[c] = (c == 0 || cnt < static_cast<uint64_t>(bud - 1)) ? 1 : 0;
+    const bool keep = live && (c == 0 || cnt < need);
+    // exclusive prefix of the keep flags: bit count below this lane within
+    // the wavefront, then the totals of the earlier wavefronts
+    const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+    const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    if (lane64 == 0) s_wtot[pass * kWavesBT + wave] = __popcll(m);
+    if (live) s_idx[c] = keep ? below : -1;
   }
   __syncthreads();
-
-  // exclusive prefix sum of the keep flags -> flattened index
-  const int seg = (C + kThreads - 1) / kThreads;
-  const int beg = tid * seg;
-  const int end = beg + seg < C ? beg + seg : C;
-  int local = 0;
-  for (int c = beg; c < end; ++c) local += s_idx[c];
-  s_part[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    int v = tid >= off ? s_part[tid - off] : 0;
-    __syncthreads();
-    s_part[tid] += v;
-    __syncthreads();
-  }
-  const int nd = s_part[kThreads - 1];
-  int run = s_part[tid] - local;
-  for (int c = beg; c < end; ++c) {
-    int kf = s_idx[c];
-    s_idx[c] = kf ? run : -1;
-    run += kf;
+  int nd = 0;
+  const int nw = ((C + kThreads - 1) / kThreads) * kWavesBT;
+  for (int w2 = 0; w2 < nw; ++w2) nd += s_wtot[w2];
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int c = pass * kThreads + tid;
+    if (c >= C) break;
+    const int i = s_idx[c];
+    if (i >= 0) {
+      int base = 0;
+      for (int w2 = 0; w2 < pass * kWavesBT + wave; ++w2) base += s_wtot[w2];
+      s_idx[c] = base + i;
+    }
   }
   __syncthreads();
 
@@ -145,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     if (i < 0) continue;
     int p = -1;
     if (c > 0) {
-      int pc = cand_parent[c0 + c];
+      int pc = s_par[c];
       p = (pc >= 0 && pc < c) ? s_idx[pc] : -1;
       if (p < 0) {
         graft::raise_flag(err, GRAFT_ERR_NOT_CLOSED);
@@ -153,18 +181,18 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
       }
     }
     s_np[i] = p;
-    s_nt[i] = cand_token[c0 + c];
+    s_nt[i] = s_ctok[c];
     s_nsrc[i] = c == 0 ? GRAFT_SRC_ROOT : GRAFT_SRC_DRAFT;
     s_low[i] = (c > 0 && s_score[c] < thresh) ? 1 : 0;
   }
   for (int r = tid; r < R; r += kThreads) {
-    int tp = ret_parent[ro + r];
+    int tp = s_rpar[r];
     int p = tp < 0 ? 0 : nd + tp;
     if (tp >= r) {
       graft::raise_flag(err, GRAFT_ERR_PARENT);
       p = 0;
     }
-    int t = ret_token[ro + r];
+    int t = s_rtok[r];
     if (t < 0 || t >= V) graft::raise_flag(err, GRAFT_ERR_TOKEN);
     s_np[nd + r] = p;
     s_nt[nd + r] = t;
@@ -223,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
       o_parent[r] = par;
       o_token[r] = tok;
       o_depth[r] = dep;
-      o_pos[r] = ctx_len[b] + dep;
+      o_pos[r] = ctx + dep;
       o_mask[r] = m;
       o_src[r] = static_cast<int8_t>(srcv);
     }

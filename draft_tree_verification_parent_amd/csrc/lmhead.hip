@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 4) void lmhead_kernel(int M, int H, int V
     for (int j = 0; j < 32; ++j)
       if (vbase + j < V) L.insert(graft::rank_key(s_t[row * TSTR + part * 32 + j], vbase + j));
     for (int j = 0; j < k; ++j) {
-      const uint64_t best = graft::group_max(L.k[0], WAVES);
+      const uint64_t best = graft::group_max<WAVES>(L.k[0]);
       if (L.k[0] == best) L.pop_front();
       if (part == 0 && m < M) part_out[(static_cast<size_t>(m) * tiles_v + tv) * k + j] = best;
     }
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_packed_kernel(int M, int H
       const int part = tid & 3;
       const int vb0 = v0 + part * 32;
       const float *src = &s_t[row * PK_TSTR + part * 32];
-      const uint64_t thr = graft::group_max(L.k[K - 1], 4);
+      const uint64_t thr = graft::group_max<4>(L.k[K - 1]);
       uint32_t pass = 0;
 #pragma unroll
       for (int j4 = 0; j4 < 32; j4 += 4) {
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_packed_kernel(int M, int H
     const int part = tid & 3;
     const int m = m0 + row;
     for (int j = 0; j < k; ++j) {
-      const uint64_t best = graft::group_max(L.k[0], 4);
+      const uint64_t best = graft::group_max<4>(L.k[0]);
       if (L.k[0] == best) L.pop_front();
       if (part == 0 && m < M) part_out[(static_cast<size_t>(m) * S + map.stream) * k + j] = best;
     }

@@ -46,8 +46,9 @@ __device__ int hash_find(const int *keys, const int *vals, int t) {
   return -1;
 }
 
-// Largest b in [0, nb) with off[b] <= r (off non-decreasing, r < off[nb]).
-__device__ int owner(const int32_t *off, int nb, int r) {
+// Largest b in [0, nb) with off[b] <= r (off non-decreasing, r < off[nb]);
+// off is an LDS copy.
+__device__ int owner(const int *off, int nb, int r) {
   int lo = 0, hi = nb - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
@@ -57,22 +58,6 @@ __device__ int owner(const int32_t *off, int nb, int r) {
   return lo;
 }
 
-// Is update row r a verified node with in-range token and ids?
-__device__ bool update_row_valid(int r, int V, int k, int B_upd, const int32_t *upd_n,
-                                 const int32_t *upd_row_off, const int32_t *upd_token,
-                                 const int32_t *upd_topk, int32_t *err, bool report) {
-  int b = owner(upd_row_off, B_upd, r);
-  int i = r - upd_row_off[b];
-  if (i >= upd_n[b] || r >= upd_row_off[b + 1]) return false;  // padding row
-  int t = upd_token[r];
-  bool ok = t >= 0 && t < V;
-  for (int j = 0; j < k; ++j) {
-    int v = upd_topk[static_cast<size_t>(r) * k + j];
-    ok = ok && v >= 0 && v < V;
-  }
-  if (!ok && report) graft::raise_flag(err, GRAFT_ERR_TOKEN);
-  return ok;
-}
 
 __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
     int32_t *__restrict__ table, int V, int k, int B_upd, const int32_t *__restrict__ upd_n,
@@ -84,42 +69,74 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
   __shared__ int s_key[kSlots];
   __shared__ int s_val[kSlots];
   __shared__ int s_tok[GRAFT_MAX_TEMPLATE_ROWS];
-  __shared__ int s_tp[GRAFT_MAX_TEMPLATE_ROWS];   // template parents, staged once
-  __shared__ int s_own[GRAFT_MAX_TEMPLATE_ROWS];  // owning request of each template row
+  __shared__ int s_tp[GRAFT_MAX_TEMPLATE_ROWS];    // template parents
+  __shared__ int s_own[GRAFT_MAX_TEMPLATE_ROWS];   // owning request of each template row
+  __shared__ int s_utok[GRAFT_MAX_UPDATE_ROWS];    // token of a valid update row, else -1
+  __shared__ signed char s_rank[GRAFT_MAX_TEMPLATE_ROWS];
   __shared__ signed char s_depth[GRAFT_MAX_TEMPLATE_ROWS];
+  __shared__ int s_toff[GRAFT_MAX_BATCH + 1];
+  __shared__ int s_root[GRAFT_MAX_BATCH];
+  __shared__ int s_uoff[GRAFT_MAX_BATCH + 1];
+  __shared__ int s_un[GRAFT_MAX_BATCH];
   __shared__ int s_maxdepth;
   const int tid = threadIdx.x;
 
+  // ---- one round of loads: offsets, roots, template structure
   for (int h = tid; h < kSlots; h += kThreads) {
     s_key[h] = -1;
     s_val[h] = -1;
   }
   if (tid == 0) s_maxdepth = 0;
+  for (int b = tid; b <= B; b += kThreads) {
+    s_toff[b] = toff[b];
+    if (b < B) s_root[b] = root_token[b];
+  }
+  for (int b = tid; b <= B_upd; b += kThreads) {
+    s_uoff[b] = upd_row_off[b];
+    if (b < B_upd) s_un[b] = upd_n[b];
+  }
   for (int t = tid; t < tmpl_rows; t += kThreads) {
     s_tp[t] = tparent[t];
-    s_own[t] = owner(toff, B, t);
+    s_rank[t] = static_cast<signed char>(min(max(trank[t], -1), 127));
   }
+  __syncthreads();
+  for (int t = tid; t < tmpl_rows; t += kThreads) s_own[t] = owner(s_toff, B, t);
   for (int b = tid; b < B_upd; b += kThreads) {
-    int cap = upd_row_off[b + 1] - upd_row_off[b];
-    if (upd_n[b] < 0 || upd_n[b] > cap) graft::raise_flag(err, GRAFT_ERR_CAPACITY);
+    const int cap = s_uoff[b + 1] - s_uoff[b];
+    const int nb = s_un[b];
+    if (nb < 0 || nb > cap) graft::raise_flag(err, GRAFT_ERR_CAPACITY);
+  }
+
+  // ---- update rows: validity (verified node, token and ids in range);
+  // last writer wins: keep the largest row index per token
+  for (int r = tid; r < upd_rows; r += kThreads) {
+    const int b = owner(s_uoff, B_upd, r);
+    const int i = r - s_uoff[b];
+    const int nb = s_un[b];
+    int tok = -1;
+    if (i < nb && r < s_uoff[b + 1]) {  // not a padding row
+      const int t = upd_token[r];
+      bool ok = t >= 0 && t < V;
+      for (int j = 0; j < k; ++j) {
+        const int v = upd_topk[static_cast<size_t>(r) * k + j];
+        ok = ok && v >= 0 && v < V;
+      }
+      if (!ok) graft::raise_flag(err, GRAFT_ERR_TOKEN);
+      else tok = t;
+    }
+    s_utok[r] = tok;
+    if (tok >= 0) hash_insert(s_key, s_val, tok, r);
   }
   __syncthreads();
 
-  // last writer wins: keep the largest row index per token
-  for (int r = tid; r < upd_rows; r += kThreads) {
-    if (update_row_valid(r, V, k, B_upd, upd_n, upd_row_off, upd_token, upd_topk, err, true))
-      hash_insert(s_key, s_val, upd_token[r], r);
-  }
-
-  // template depths (request-local parents must precede their child)
+  // ---- template depths (request-local parents must precede their child)
   for (int t = tid; t < tmpl_rows; t += kThreads) {
-    int b = s_own[t];
-    int base = toff[b];
+    const int base = s_toff[s_own[t]];
     int cur = t - base;
     int d = 1;
     bool ok = true;
     while (true) {
-      int p = s_tp[base + cur];
+      const int p = s_tp[base + cur];
       if (p < 0) break;
       if (p >= cur) {
         ok = false;
@@ -138,33 +155,24 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
   }
   __syncthreads();
 
-  // copy the winning rows into the table (these rows are never read below)
-  for (int r = tid; r < upd_rows; r += kThreads) {
-    if (!update_row_valid(r, V, k, B_upd, upd_n, upd_row_off, upd_token, upd_topk, err, false))
-      continue;
-    int t = upd_token[r];
-    if (hash_find(s_key, s_val, t) != r) continue;
-    for (int j = 0; j < k; ++j)
-      table[static_cast<size_t>(t) * k + j] = upd_topk[static_cast<size_t>(r) * k + j];
-  }
-
-  // expand the templates level by level
+  // ---- expand the templates level by level; a just-updated token's row is
+  // read from the update list, any other from the table (never memory this
+  // launch writes)
   const int maxd = s_maxdepth;
   for (int level = 1; level <= maxd; ++level) {
     for (int t = tid; t < tmpl_rows; t += kThreads) {
       if (s_depth[t] != level) continue;
-      int b = s_own[t];
-      int base = toff[b];
-      int p = s_tp[t];
-      int src = p < 0 ? root_token[b] : s_tok[base + p];
-      int rank = trank[t];
+      const int b = s_own[t];
+      const int base = s_toff[b];
+      const int p = s_tp[t];
+      const int src = p < 0 ? s_root[b] : s_tok[base + p];
+      const int rank = s_rank[t];
       int tok = -1;
       if (rank < 0 || rank >= k) {
         graft::raise_flag(err, GRAFT_ERR_RANK);
       } else if (src >= 0 && src < V) {
-        int w = hash_find(s_key, s_val, src);
-        tok = w >= 0 ? upd_topk[static_cast<size_t>(w) * k + rank]
-                     : table[static_cast<size_t>(src) * k + rank];
+        const int w = hash_find(s_key, s_val, src);
+        tok = w >= 0 ? upd_topk[static_cast<size_t>(w) * k + rank] : table[static_cast<size_t>(src) * k + rank];
         if (tok < 0 || tok >= V) {
           graft::raise_flag(err, GRAFT_ERR_TOKEN);
           tok = -1;
@@ -177,6 +185,15 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
     __syncthreads();
   }
   for (int t = tid; t < tmpl_rows; t += kThreads) ret_token[t] = s_depth[t] > 0 ? s_tok[t] : -1;
+
+  // ---- copy the winning rows into the table (rows read above come from the
+  // update list for these tokens, so the order does not matter)
+  for (int r = tid; r < upd_rows; r += kThreads) {
+    const int t = s_utok[r];
+    if (t < 0 || hash_find(s_key, s_val, t) != r) continue;
+    for (int j = 0; j < k; ++j)
+      table[static_cast<size_t>(t) * k + j] = upd_topk[static_cast<size_t>(r) * k + j];
+  }
 }
 
 }  // namespace
@@ -192,12 +209,12 @@ extern "C" int graft_table_update_retrieve(int32_t *table, int V, int k, int B_u
   using graft::fail;
   if (V <= 0 || k < 1 || k > GRAFT_MAX_K) return fail(GRAFT_EINVAL, "table_update_retrieve: V=%d k=%d", V, k);
   if (!table) return fail(GRAFT_EINVAL, "table_update_retrieve: table is NULL");
-  if (B_upd < 0 || upd_rows < 0 || upd_rows > GRAFT_MAX_UPDATE_ROWS)
-    return fail(GRAFT_EINVAL, "table_update_retrieve: B_upd=%d upd_rows=%d (max %d)", B_upd, upd_rows,
-                GRAFT_MAX_UPDATE_ROWS);
-  if (B < 0 || tmpl_rows < 0 || tmpl_rows > GRAFT_MAX_TEMPLATE_ROWS)
-    return fail(GRAFT_EINVAL, "table_update_retrieve: B=%d tmpl_rows=%d (max %d)", B, tmpl_rows,
-                GRAFT_MAX_TEMPLATE_ROWS);
+  if (B_upd < 0 || B_upd > GRAFT_MAX_BATCH || upd_rows < 0 || upd_rows > GRAFT_MAX_UPDATE_ROWS)
+    return fail(GRAFT_EINVAL, "table_update_retrieve: B_upd=%d (max %d) upd_rows=%d (max %d)", B_upd,
+                GRAFT_MAX_BATCH, upd_rows, GRAFT_MAX_UPDATE_ROWS);
+  if (B < 0 || B > GRAFT_MAX_BATCH || tmpl_rows < 0 || tmpl_rows > GRAFT_MAX_TEMPLATE_ROWS)
+    return fail(GRAFT_EINVAL, "table_update_retrieve: B=%d (max %d) tmpl_rows=%d (max %d)", B, GRAFT_MAX_BATCH,
+                tmpl_rows, GRAFT_MAX_TEMPLATE_ROWS);
   if (B_upd == 0) upd_rows = 0;
   if (B == 0) tmpl_rows = 0;
   if (upd_rows > 0 && (!upd_n || !upd_row_off || !upd_token || !upd_topk))

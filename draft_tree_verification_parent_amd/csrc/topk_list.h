@@ -6,6 +6,8 @@
 // comes back as +0; the two compare equal).  Key 0 is the empty slot.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace graft {
@@ -44,12 +46,48 @@ struct TopKeys {
   }
 };
 
-// Largest key over the lanes of xor-groups of `width` lanes (width a power of
-// two <= 64); every lane of the group gets the result.
-__device__ inline uint64_t group_max(uint64_t x, int width) {
-  for (int off = 1; off < width; off <<= 1) {
-    const uint64_t o = __shfl_xor(x, off);
-    x = o > x ? o : x;
+// 32-bit lane exchanges without LDS: DPP within a row of 16 lanes, the
+// gfx950 row-swap permutes across rows.  Every lane of a group ends up
+// paired with a lane of the other half of its group, which is all a
+// max-reduction needs.
+namespace lanes {
+constexpr int kXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kHalfMirror = 0x141; // lane i <-> 7 - i within 8 lanes
+constexpr int kMirror = 0x140;     // lane i <-> 15 - i within 16 lanes
+template <int CTRL>
+__device__ inline uint32_t dpp(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, false));
+}
+}  // namespace lanes
+
+__device__ inline uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Largest key over aligned groups of W lanes (W a power of two <= 64); every
+// lane of the group gets the result.
+template <int W>
+__device__ inline uint64_t group_max(uint64_t x) {
+  auto step_dpp = [](uint64_t v, auto ctrl_tag) {
+    constexpr int C = decltype(ctrl_tag)::value;
+    const uint32_t lo = lanes::dpp<C>(static_cast<uint32_t>(v));
+    const uint32_t hi = lanes::dpp<C>(static_cast<uint32_t>(v >> 32));
+    return max_u64(v, (static_cast<uint64_t>(hi) << 32) | lo);
+  };
+  if constexpr (W >= 2) x = step_dpp(x, std::integral_constant<int, lanes::kXor1>{});
+  if constexpr (W >= 4) x = step_dpp(x, std::integral_constant<int, lanes::kXor2>{});
+  if constexpr (W >= 8) x = step_dpp(x, std::integral_constant<int, lanes::kHalfMirror>{});
+  if constexpr (W >= 16) x = step_dpp(x, std::integral_constant<int, lanes::kMirror>{});
+  if constexpr (W >= 32) {
+    const auto lo = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x), false, false);
+    const auto hi =
+        __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(x >> 32), static_cast<uint32_t>(x >> 32), false, false);
+    x = max_u64((static_cast<uint64_t>(hi[0]) << 32) | lo[0], (static_cast<uint64_t>(hi[1]) << 32) | lo[1]);
+  }
+  if constexpr (W >= 64) {
+    const auto lo = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x), false, false);
+    const auto hi =
+        __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(x >> 32), static_cast<uint32_t>(x >> 32), false, false);
+    x = max_u64((static_cast<uint64_t>(hi[0]) << 32) | lo[0], (static_cast<uint64_t>(hi[1]) << 32) | lo[1]);
   }
   return x;
 }
@@ -61,7 +99,7 @@ __device__ inline uint64_t wave_extract(TopKeys<K> &L, int k) {
   const int lane = threadIdx.x & 63;
   uint64_t out = 0;
   for (int j = 0; j < k; ++j) {
-    const uint64_t best = group_max(L.k[0], 64);
+    const uint64_t best = group_max<64>(L.k[0]);
     if (L.k[0] == best) L.pop_front();
     if (lane == j) out = best;
   }

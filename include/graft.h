@@ -55,6 +55,7 @@ typedef void *graft_stream;
 #define GRAFT_MAX_CAND 2048
 #define GRAFT_MAX_UPDATE_ROWS 4096
 #define GRAFT_MAX_TEMPLATE_ROWS 4096
+#define GRAFT_MAX_BATCH 1024 /* requests per table update / retrieval call */
 
 /* return status */
 #define GRAFT_OK 0
@@ -109,7 +110,9 @@ int graft_version(void);
  *   GRAFT_MAX_TEMPLATE_ROWS.  Invalid links yield ret_token = -1 with
  *   ERR_PARENT / ERR_RANK / ERR_TOKEN.
  * Either part may be empty (B_upd = 0 or upd_rows = 0; B = 0 or
- * tmpl_rows = 0).  One workgroup; calls that overlap on a table race.
+ * tmpl_rows = 0).  B, B_upd <= GRAFT_MAX_BATCH (their offsets are staged in
+ * LDS); larger batches return GRAFT_EINVAL.  One workgroup; calls that
+ * overlap on a table race.
  */
 int graft_table_update_retrieve(int32_t *table, int V, int k,
                                 int B_upd, const int32_t *upd_n, const int32_t *upd_row_off,

@@ -101,6 +101,11 @@ def test_host_argument_validation_launches_nothing(native):
                                          None, 0, None, None, None) == E
     assert L.graft_table_update_retrieve(1, 100, 8, 0, None, None, 0, None, None, 0, None, None,
                                          None, None, 0, None, None, None) == 0
+    # batches above GRAFT_MAX_BATCH requests are rejected before any launch
+    assert L.graft_table_update_retrieve(1, 100, 8, 1025, 1, 1, 10, 1, 1, 0, None, None, None,
+                                         None, 0, None, None, None) == E
+    assert L.graft_table_update_retrieve(1, 100, 8, 0, None, None, 0, None, None, 1025, 1, 1, 1,
+                                         1, 10, 1, None, None) == E
     # accept
     assert L.graft_accept(1, 1, 1, 1, 1, 1, 0, 1, 1, 1, None, None) == E
     assert L.graft_accept(0, None, None, None, None, None, 8, None, None, None, None, None) == 0
