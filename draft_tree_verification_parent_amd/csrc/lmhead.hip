@@ -226,9 +226,11 @@ constexpr int PK_NS = 3;                    // LDS ring stages
 constexpr int PK_WB = PK_BV * PK_KC * 2;    // 32 KB stage image of W
 constexpr int PK_HB = BM * PK_KC * 2;       // 16 KB hidden chunk
 constexpr int PK_SB = PK_WB + PK_HB;        // one ring stage
-constexpr int PK_WI = PK_WB / 1024 / kWaves;  // W DMA instructions per wave per stage (8)
-constexpr int PK_HI = PK_HB / 1024 / kWaves;  // hidden DMA instructions per wave per stage (4)
 constexpr int PK_GRID = 256;                // persistent workgroups (one per MI355X CU)
+#ifndef GRAFT_PK_WAVES
+#define GRAFT_PK_WAVES 4
+#endif
+constexpr int PK_WAVES = GRAFT_PK_WAVES;    // wavefronts per packed-path workgroup
 constexpr int PK_TSTR = PK_BV + 4;          // floats per row of the staged logit tile
 static_assert(BM * PK_TSTR * 4 <= PK_SB, "logit tile must fit in one ring stage");
 
@@ -292,13 +294,26 @@ __device__ __host__ inline PkMap pk_map(int block, int T) {
   return r;
 }
 
-template <bool FUSED, int K>
-__global__ __launch_bounds__(kThreads, 1) void lmhead_packed_kernel(int M, int H, int V, int k,
-                                                                  const graft_bf16 *__restrict__ hidden,
-                                                                  const unsigned char *__restrict__ wpk,
-                                                                  float *__restrict__ logits,
-                                                                  uint64_t *__restrict__ part_out, int tiles_m,
-                                                                  int tiles_v) {
+// PW wavefronts per workgroup; wavefront w owns vocabulary rows
+// [w * 128 / PW, (w + 1) * 128 / PW) of each tile and all 64 hidden rows.
+// Larger per-wave tiles need fewer LDS fragment reads per MFMA (2 waves:
+// 8 reads per 16 MFMAs; 4 waves: 6 per 8).
+template <bool FUSED, int K, int PW>
+__global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H, int V, int k,
+                                                                 const graft_bf16 *__restrict__ hidden,
+                                                                 const unsigned char *__restrict__ wpk,
+                                                                 float *__restrict__ logits,
+                                                                 uint64_t *__restrict__ part_out, int tiles_m,
+                                                                 int tiles_v) {
+  constexpr int NT = PW * 64;
+  constexpr int VW = PK_BV / PW;      // vocabulary rows per wave
+  constexpr int VBW = VW / 16;        // 16-row MFMA blocks per wave
+  constexpr int WI = PK_WB / 1024 / PW;  // W DMA instructions per wave per stage
+  constexpr int HI = PK_HB / 1024 / PW;  // hidden DMA instructions per wave per stage
+  constexpr int TPR = NT / BM;        // epilogue threads per logit row
+  constexpr int VPT = PK_BV / TPR;    // tile entries per epilogue thread
+  constexpr int GPT = VPT / 8;        // groups of 8 entries per epilogue thread
+  using PassT = typename std::conditional<(VPT > 32), uint64_t, uint32_t>::type;
   __shared__ __attribute__((aligned(1024))) unsigned char sm[PK_NS * PK_SB];
   const PkMap map = pk_map(blockIdx.x, tiles_m);
   if (map.stream < 0) return;
@@ -318,12 +333,12 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_packed_kernel(int M, int H
 
   // loop-invariant DMA source offsets: W images are copied linearly; hidden
   // row r (clamped to M - 1) lands swizzled like the images
-  unsigned wo[PK_WI], ho[PK_HI];
+  unsigned wo[WI], ho[HI];
 #pragma unroll
-  for (int i = 0; i < PK_WI; ++i) wo[i] = ((wave * PK_WI + i) * 64 + lane) * 16;
+  for (int i = 0; i < WI; ++i) wo[i] = ((wave * WI + i) * 64 + lane) * 16;
 #pragma unroll
-  for (int i = 0; i < PK_HI; ++i) {
-    const int r = 4 * (wave * PK_HI + i) + (lane >> 4);
+  for (int i = 0; i < HI; ++i) {
+    const int r = 4 * (wave * HI + i) + (lane >> 4);
     const int m = min(m0 + r, M - 1);
     ho[i] = static_cast<unsigned>(m) * H * 2 + (((lane & 15) ^ (r & 15)) * 16);
   }
@@ -333,17 +348,17 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_packed_kernel(int M, int H
     const int c = q - (q / nch) * nch;
     const unsigned char *wsrc = wpk + (static_cast<size_t>(tv) * nch + c) * PK_WB;
     const unsigned char *hsrc = reinterpret_cast<const unsigned char *>(hidden) + c * PK_KC * 2;
-    const unsigned wl = sbase + st * PK_SB + wave * PK_WI * 1024;
-    const unsigned hl = sbase + st * PK_SB + PK_WB + wave * PK_HI * 1024;
+    const unsigned wl = sbase + st * PK_SB + wave * WI * 1024;
+    const unsigned hl = sbase + st * PK_SB + PK_WB + wave * HI * 1024;
 #pragma unroll
-    for (int i = 0; i < PK_HI; ++i) lds_dma16_cached(hl + i * 1024, hsrc, ho[i]);
+    for (int i = 0; i < HI; ++i) lds_dma16_cached(hl + i * 1024, hsrc, ho[i]);
 #pragma unroll
-    for (int i = 0; i < PK_WI; ++i) lds_dma16(wl + i * 1024, wsrc, wo[i]);
+    for (int i = 0; i < WI; ++i) lds_dma16(wl + i * 1024, wsrc, wo[i]);
   };
 
-  f32x4 acc[2][4];
+  f32x4 acc[VBW][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < VBW; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   graft::TopKeys<K> L;
@@ -353,7 +368,7 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_packed_kernel(int M, int H
   if (Q > 1) issue(1);
   for (int q = 0; q < Q; ++q) {
     // chunk q has landed once only chunk q + 1's DMAs may still be in flight
-    if (q + 1 < Q) ring_barrier<PK_WI + PK_HI>();
+    if (q + 1 < Q) ring_barrier<WI + HI>();
     else ring_barrier<0>();
     if (q + 2 < Q) issue(q + 2);  // into the stage chunk q - 1 used
     const unsigned char *ws = sm + (q % PK_NS) * PK_SB;
@@ -361,15 +376,15 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_packed_kernel(int M, int H
 #pragma unroll
     for (int s = 0; s < PK_KC / 32; ++s) {
       const int P = s * 4 + g;  // 16-byte piece of the lane's 8 k values
-      bf16x8 a[2], bh[4];
+      bf16x8 a[VBW], bh[4];
 #pragma unroll
-      for (int vb = 0; vb < 2; ++vb)
-        a[vb] = *reinterpret_cast<const bf16x8 *>(ws + (wave * 32 + vb * 16 + l16) * 256 + (P ^ l16) * 16);
+      for (int vb = 0; vb < VBW; ++vb)
+        a[vb] = *reinterpret_cast<const bf16x8 *>(ws + (wave * VW + vb * 16 + l16) * 256 + (P ^ l16) * 16);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
         bh[mb] = *reinterpret_cast<const bf16x8 *>(hs + (mb * 16 + l16) * 256 + (P ^ l16) * 16);
 #pragma unroll
-      for (int vb = 0; vb < 2; ++vb)
+      for (int vb = 0; vb < VBW; ++vb)
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
           acc[vb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[vb], bh[mb], acc[vb][mb], 0, 0, 0);
@@ -384,42 +399,78 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_packed_kernel(int M, int H
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int vb = 0; vb < 2; ++vb) {
-        *reinterpret_cast<f32x4 *>(&s_t[(mb * 16 + l16) * PK_TSTR + wave * 32 + vb * 16 + 4 * g]) = acc[vb][mb];
+      for (int vb = 0; vb < VBW; ++vb) {
+        *reinterpret_cast<f32x4 *>(&s_t[(mb * 16 + l16) * PK_TSTR + wave * VW + vb * 16 + 4 * g]) = acc[vb][mb];
         acc[vb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     __syncthreads();
     if constexpr (FUSED) {
-      // 4 consecutive threads per row, 32 entries each, into the persistent
-      // lists.  An entry whose key is not above the largest of the row's four
-      // k-th keys cannot reach the row's top k (k keys of the row already
-      // beat it), so only the few entries above that threshold are inserted.
-      const int row = tid >> 2;
-      const int part = tid & 3;
-      const int vb0 = v0 + part * 32;
-      const float *src = &s_t[row * PK_TSTR + part * 32];
-      const uint64_t thr = graft::group_max<4>(L.k[K - 1]);
-      uint32_t pass = 0;
+      // TPR consecutive threads per row, VPT entries each, into the
+      // persistent lists.  Only entries that can still reach the row's top k
+      // are inserted: an entry below the largest of the row's listed k-th
+      // keys is beaten by k listed keys, and an entry below the k-th largest
+      // of the tile row's 16 group maxima (groups of 8 entries) is beaten by
+      // k entries of this tile.  The test is done on the float values (NaN
+      // always passes, as its key ranks it); the insert compares keys.
+      const int row = tid / TPR;
+      const int part = tid - row * TPR;
+      const int vb0 = v0 + part * VPT;
+      const float *src = &s_t[row * PK_TSTR + part * VPT];
+      float xv[VPT];
 #pragma unroll
-      for (int j4 = 0; j4 < 32; j4 += 4) {
+      for (int j4 = 0; j4 < VPT; j4 += 4) {
         const float4 x = *reinterpret_cast<const float4 *>(src + j4);
-        const float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int j = j4 + i;
-          const bool in = (vb0 + j < V) & (graft::rank_key(xs[i], vb0 + j) > thr);
-          pass |= static_cast<uint32_t>(in) << j;
-        }
+        xv[j4] = vb0 + j4 < V ? x.x : -INFINITY;
+        xv[j4 + 1] = vb0 + j4 + 1 < V ? x.y : -INFINITY;
+        xv[j4 + 2] = vb0 + j4 + 2 < V ? x.z : -INFINITY;
+        xv[j4 + 3] = vb0 + j4 + 3 < V ? x.w : -INFINITY;
       }
-      while (pass != 0) {  // entries re-read from LDS: no dynamic register indexing
-        const int j = __builtin_ctz(pass);
-        pass &= pass - 1;
-        L.insert(graft::rank_key(src[j], vb0 + j));
+      float gm[GPT];
+#pragma unroll
+      for (int q8 = 0; q8 < GPT; ++q8) {
+        float m8 = xv[8 * q8];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) m8 = fmaxf(m8, xv[8 * q8 + e]);
+        gm[q8] = m8;
+      }
+      // k-th largest of the row's 16 maxima: k rounds of remove-the-largest
+      // (equal maxima removed together only lower the bound, which keeps it
+      // valid)
+      float gk = -INFINITY;
+      for (int r = 0; r < k; ++r) {
+        float lm = gm[0];
+#pragma unroll
+        for (int q8 = 1; q8 < GPT; ++q8) lm = fmaxf(lm, gm[q8]);
+        const float best = graft::group_maxf<TPR>(lm);
+#pragma unroll
+        for (int q8 = 0; q8 < GPT; ++q8) gm[q8] = gm[q8] == best ? -INFINITY : gm[q8];
+        gk = best;
+      }
+      const uint64_t thr = graft::group_max<TPR>(L.k[K - 1]);
+      const float tv = thr != 0 ? graft::key_value(thr) : -INFINITY;
+      const float bound = fmaxf(gk, tv);
+      PassT pass = 0;
+#pragma unroll
+      for (int j = 0; j < VPT; ++j) pass |= static_cast<PassT>(!(xv[j] < bound) & (vb0 + j < V)) << j;
+      // entries re-read from LDS (no dynamic register indexing); the next
+      // entry's read is issued before the current insert
+      if (pass != 0) {
+        int j = static_cast<int>(__builtin_ctzll(pass));
+        float vj = src[j];
+        while (true) {
+          pass &= pass - 1;
+          const int jn = pass != 0 ? static_cast<int>(__builtin_ctzll(pass)) : j;
+          const float vn = src[jn];
+          L.insert(graft::rank_key(vj, vb0 + j));
+          if (pass == 0) break;
+          j = jn;
+          vj = vn;
+        }
       }
     } else {
       // coalesced rows: 32 float4 per row
       const bool vec = (V & 3) == 0;
-      for (int e = tid; e < BM * (PK_BV / 4); e += kThreads) {
+      for (int e = tid; e < BM * (PK_BV / 4); e += NT) {
         const int row = e / (PK_BV / 4);
         const int c4 = (e - row * (PK_BV / 4)) * 4;
         const int m = m0 + row;
@@ -437,11 +488,11 @@ __global__ __launch_bounds__(kThreads, 1) void lmhead_packed_kernel(int M, int H
   }
   if constexpr (FUSED) {
     // k best keys of each row over this workgroup's tiles (0 = no entry)
-    const int row = tid >> 2;
-    const int part = tid & 3;
+    const int row = tid / TPR;
+    const int part = tid - row * TPR;
     const int m = m0 + row;
     for (int j = 0; j < k; ++j) {
-      const uint64_t best = graft::group_max<4>(L.k[0]);
+      const uint64_t best = graft::group_max<TPR>(L.k[0]);
       if (L.k[0] == best) L.pop_front();
       if (part == 0 && m < M) part_out[(static_cast<size_t>(m) * S + map.stream) * k + j] = best;
     }
@@ -536,7 +587,7 @@ extern "C" int graft_lmhead_topk(int M, int H, int V, int k, const graft_bf16 *h
     auto launch = [&](auto fused_tag, auto k_tag, uint64_t *pk) {
       constexpr bool F = decltype(fused_tag)::value;
       constexpr int Kv = decltype(k_tag)::value;
-      hipLaunchKernelGGL((lmhead_packed_kernel<F, Kv>), dim3(PK_GRID), dim3(kThreads), 0, s, M, H, V, F ? k : 0,
+      hipLaunchKernelGGL((lmhead_packed_kernel<F, Kv, PK_WAVES>), dim3(PK_GRID), dim3(PK_WAVES * 64), 0, s, M, H, V, F ? k : 0,
                          hidden, wpk, F ? nullptr : logits, pk, tiles_m, tiles_v);
     };
     if (fused) {
