@@ -202,7 +202,7 @@ def main():
     traffic = measured_traffic(wkey)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": (f"lmhead_packed_kernel<true,{8 if ri.k <= 8 else 16}> + "
+                "kernel": (f"lmhead_packed_kernel<true,{8 if ri.k <= 8 else 16},8> + "
                            f"topk_merge_kernel<{8 if ri.k <= 8 else 16}> (one graft_lmhead_topk call, "
                            f"packed weights)"),
                 "algorithmic_bytes_per_launch": lm_bytes,

@@ -228,7 +228,7 @@ constexpr int PK_HB = BM * PK_KC * 2;       // 16 KB hidden chunk
 constexpr int PK_SB = PK_WB + PK_HB;        // one ring stage
 constexpr int PK_GRID = 256;                // persistent workgroups (one per MI355X CU)
 #ifndef GRAFT_PK_WAVES
-#define GRAFT_PK_WAVES 4
+#define GRAFT_PK_WAVES 8
 #endif
 constexpr int PK_WAVES = GRAFT_PK_WAVES;    // wavefronts per packed-path workgroup
 constexpr int PK_TSTR = PK_BV + 4;          // floats per row of the staged logit tile

@@ -92,12 +92,13 @@ __device__ inline uint64_t group_max(uint64_t x) {
   return x;
 }
 
-// Largest float over aligned groups of W <= 4 lanes (every lane of the group gets it).
+// Largest float over aligned groups of W <= 8 lanes (every lane of the group gets it).
 template <int W>
 __device__ inline float group_maxf(float x) {
-  static_assert(W == 1 || W == 2 || W == 4, "groups of 1, 2 or 4 lanes");
+  static_assert(W == 1 || W == 2 || W == 4 || W == 8, "groups of 1, 2, 4 or 8 lanes");
   if constexpr (W >= 2) x = fmaxf(x, __uint_as_float(lanes::dpp<lanes::kXor1>(__float_as_uint(x))));
   if constexpr (W >= 4) x = fmaxf(x, __uint_as_float(lanes::dpp<lanes::kXor2>(__float_as_uint(x))));
+  if constexpr (W >= 8) x = fmaxf(x, __uint_as_float(lanes::dpp<lanes::kHalfMirror>(__float_as_uint(x))));
   return x;
 }
 
