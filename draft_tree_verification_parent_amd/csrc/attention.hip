@@ -45,7 +45,9 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int KCH = 64;      // keys per staged chunk (four 16-key MFMA blocks)
-constexpr int NS = 4;        // LDS ring stages
+constexpr int NS_SHORT = 4;  // LDS ring stages: one 128 KB workgroup per CU
+constexpr int NS_LONG = 2;   // two 64 KB workgroups per CU (long key ranges)
+constexpr int LONG_KEYS = 16384;  // key range from which the 2-stage ring is used
 constexpr int MIN_SPLIT = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -152,7 +154,7 @@ __device__ inline bool request_ok(const Params &P, int b, int &ctx, int &n) {
   return ok;
 }
 
-template <int D, int RBW>
+template <int D, int RBW, int NS>
 __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
   using TL = Tile<D>;
   constexpr int DS = D / 32;  // MFMA k-steps over the head dim
@@ -459,7 +461,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(Params P) {
 }
 
 struct Plan {
-  int rbw, row_groups, rows_per_wg, rows_cap, split_len, nsplit;
+  int rbw, ns, row_groups, rows_per_wg, rows_cap, split_len, nsplit;
   size_t ws_bytes;
 };
 
@@ -469,19 +471,27 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int max_n) {
   const int rows = max_n * G;
   const int rb = (rows + 15) / 16;
   const long long L = static_cast<long long>(max_ctx) + max_n;
-  // fewest row groups that fit (at most 3 row blocks per wave): every group
-  // re-reads the K/V tiles from LDS once per wave, so more rows per wave
-  // means less LDS traffic per query row
-  if (rb <= kWaves) p.rbw = 1;
+  // Row blocks per wavefront.  With few (request, KV head) units a
+  // workgroup's time is latency-bound and more, lighter workgroups win
+  // (measured), so one row block per wave is used as long as that makes at
+  // most two row groups (each group re-reads the K/V tiles).  Otherwise the
+  // fewest row groups (at most 3 row blocks per wave: 4 spill at d = 128).
+  const int rg1 = (rows + kWaves * 16 - 1) / (kWaves * 16);
+  if (rg1 <= 2 && static_cast<long long>(B) * Hkv * rg1 < 256) p.rbw = 1;
+  else if (rb <= kWaves) p.rbw = 1;
   else if (rb <= 2 * kWaves) p.rbw = 2;
   else p.rbw = 3;
+  // Long key ranges with one row block per wave use the 2-stage ring: two
+  // 64 KB workgroups share a CU and overlap each other's stalls.
+  p.ns = (p.rbw == 1 && L >= LONG_KEYS) ? NS_LONG : NS_SHORT;
   p.rows_per_wg = kWaves * p.rbw * 16;
   p.row_groups = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
   p.rows_cap = rb * 16;
-  // one workgroup per CU (the LDS ring takes most of a CU's LDS): split the
-  // keys so that about 256 workgroups run at once
+  // split the keys so that about 256 (one per CU) or 512 (two per CU)
+  // workgroups run at once
   const long long units = static_cast<long long>(B) * Hkv * p.row_groups;
-  long long want = units > 0 ? (256 + units - 1) / units : 1;
+  const long long target = p.ns == NS_LONG ? 512 : 256;
+  long long want = units > 0 ? (target + units - 1) / units : 1;
   if (want < 1) want = 1;
   long long len = (L + want - 1) / want;
   len = (len + 31) / 32 * 32;
@@ -499,11 +509,14 @@ bool shape_ok(int B, int Hq, int Hkv, int d, int max_ctx, int max_n) {
 
 template <int D>
 void launch(const Plan &pl, const Params &P, dim3 grid, hipStream_t s) {
-  switch (pl.rbw) {
-    case 1: hipLaunchKernelGGL((tree_attn_kernel<D, 1>), grid, dim3(kThreads), 0, s, P); break;
-    case 2: hipLaunchKernelGGL((tree_attn_kernel<D, 2>), grid, dim3(kThreads), 0, s, P); break;
-    default: hipLaunchKernelGGL((tree_attn_kernel<D, 3>), grid, dim3(kThreads), 0, s, P); break;
-  }
+  if (pl.rbw == 1 && pl.ns == NS_LONG)
+    hipLaunchKernelGGL((tree_attn_kernel<D, 1, NS_LONG>), grid, dim3(kThreads), 0, s, P);
+  else if (pl.rbw == 1)
+    hipLaunchKernelGGL((tree_attn_kernel<D, 1, NS_SHORT>), grid, dim3(kThreads), 0, s, P);
+  else if (pl.rbw == 2)
+    hipLaunchKernelGGL((tree_attn_kernel<D, 2, NS_SHORT>), grid, dim3(kThreads), 0, s, P);
+  else
+    hipLaunchKernelGGL((tree_attn_kernel<D, 3, NS_SHORT>), grid, dim3(kThreads), 0, s, P);
   if (pl.nsplit > 1) {
     constexpr int RPB = 256 / (D / 4);
     dim3 mg((pl.rows_cap + RPB - 1) / RPB, P.Hkv, P.B);
