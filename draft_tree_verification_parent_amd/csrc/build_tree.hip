@@ -10,13 +10,16 @@
 // (Graft page, section 4, batched-serving paragraph).
 //
 // One workgroup of 512 threads per request.  Every input array is staged in
-// LDS by one round of loads.  Ranking is a rank count: one candidate per
-// thread compares its 64-bit key with every other key (broadcast LDS reads,
-// one unsigned compare per pair), and a wavefront stops as soon as each of
-// its candidates already has budget-1 better ones.  Flattened indices come
-// from a ballot / bit-count prefix scan.  The <= 64 flattened nodes map one
-// per lane of wave 0, where ancestor masks and depths come from six rounds
-// of pointer jumping over the parent links.
+// LDS by one round of loads.  Ranking works on unique 64-bit keys: each
+// wavefront sorts its blocks of 64 keys in registers (bitonic network over
+// DPP and row-swap permutes) and keeps the 64 largest; pairwise bitonic
+// merges across wavefronts give the request's 64 largest keys, and with
+// them the smallest key within the budget, against which every candidate
+// is tested.  Flattened indices come from a ballot / bit-count prefix scan.
+// The <= 64 flattened nodes map one per lane of wave 0, where ancestor masks
+// and depths come from six rounds of pointer jumping over the parent links;
+// static replacement looks up the table in rounds, one per link of the
+// longest chain of replaced nodes.
 #include "common.h"
 
 namespace {
@@ -37,6 +40,90 @@ __device__ void write_padding(int from, int to, int32_t *parent, int32_t *token,
   }
 }
 
+// Value of the lane whose index differs from this lane's in bit J, without
+// LDS traffic: DPP quad permutes (J = 1, 2), DPP row rotates (J = 4, 8;
+// lane i reads lane i - N mod 16 under a rotate by N) and the gfx950
+// row-swap permutes (J = 16, 32), which hand back the even and the odd
+// half of each pair of rows.
+template <int J>
+__device__ inline uint32_t lane_xor32(uint32_t x, int lane) {
+  const int v = static_cast<int>(x);
+  if constexpr (J == 1) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (J == 2) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (J == 4) {
+    const int up = __builtin_amdgcn_update_dpp(0, v, 0x12C, 0xF, 0xF, false);  // lane i + 4
+    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // lane i - 4
+    return static_cast<uint32_t>((lane & 4) ? dn : up);
+  } else if constexpr (J == 8) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    static_assert(J == 32, "lane distance 1..32");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+
+template <int J>
+__device__ inline uint64_t lane_xor(uint64_t x, int lane) {
+  const uint32_t lo = lane_xor32<J>(static_cast<uint32_t>(x), lane);
+  const uint32_t hi = lane_xor32<J>(static_cast<uint32_t>(x >> 32), lane);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// One compare-exchange stage of a bitonic network over the 64 lanes: pairs
+// (i, i ^ J); within K-blocks whose index bit K is clear the lower lane keeps
+// the larger key (the smaller when the whole network sorts ascending).
+template <int K, int J>
+__device__ inline uint64_t bitonic_step(uint64_t x, int lane, bool desc) {
+  const uint64_t y = lane_xor<J>(x, lane);
+  const bool keep_max = (((lane & K) == 0) == ((lane & J) == 0)) == desc;
+  return keep_max ? (x > y ? x : y) : (x < y ? x : y);
+}
+
+// Sorts the 64 keys of a wavefront, largest in lane 0 when desc, smallest
+// otherwise.
+__device__ inline uint64_t wave_sort(uint64_t x, int lane, bool desc) {
+  x = bitonic_step<2, 1>(x, lane, desc);
+  x = bitonic_step<4, 2>(x, lane, desc);
+  x = bitonic_step<4, 1>(x, lane, desc);
+  x = bitonic_step<8, 4>(x, lane, desc);
+  x = bitonic_step<8, 2>(x, lane, desc);
+  x = bitonic_step<8, 1>(x, lane, desc);
+  x = bitonic_step<16, 8>(x, lane, desc);
+  x = bitonic_step<16, 4>(x, lane, desc);
+  x = bitonic_step<16, 2>(x, lane, desc);
+  x = bitonic_step<16, 1>(x, lane, desc);
+  x = bitonic_step<32, 16>(x, lane, desc);
+  x = bitonic_step<32, 8>(x, lane, desc);
+  x = bitonic_step<32, 4>(x, lane, desc);
+  x = bitonic_step<32, 2>(x, lane, desc);
+  x = bitonic_step<32, 1>(x, lane, desc);
+  x = bitonic_step<64, 32>(x, lane, desc);
+  x = bitonic_step<64, 16>(x, lane, desc);
+  x = bitonic_step<64, 8>(x, lane, desc);
+  x = bitonic_step<64, 4>(x, lane, desc);
+  x = bitonic_step<64, 2>(x, lane, desc);
+  return bitonic_step<64, 1>(x, lane, desc);
+}
+
+// Top 64 of two sorted blocks, a in direction desc and b in the opposite
+// one: their lane-wise maximum is a bitonic sequence holding the 64 largest
+// keys of both, which the last six stages of the network then sort.
+__device__ inline uint64_t top64_merge(uint64_t a, uint64_t b, int lane, bool desc) {
+  uint64_t x = a > b ? a : b;
+  x = bitonic_step<64, 32>(x, lane, desc);
+  x = bitonic_step<64, 16>(x, lane, desc);
+  x = bitonic_step<64, 8>(x, lane, desc);
+  x = bitonic_step<64, 4>(x, lane, desc);
+  x = bitonic_step<64, 2>(x, lane, desc);
+  return bitonic_step<64, 1>(x, lane, desc);
+}
+
 __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     int mode, const int32_t *__restrict__ cand_parent, const int32_t *__restrict__ cand_token,
     const float *__restrict__ cand_score, const int32_t *__restrict__ cand_off, int max_cand,
@@ -48,11 +135,12 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     int32_t *__restrict__ o_depth, int32_t *__restrict__ o_pos, uint64_t *__restrict__ o_mask,
     int8_t *__restrict__ o_src, int32_t *__restrict__ err) {
   __shared__ float s_score[GRAFT_MAX_CAND];
-  __shared__ __attribute__((aligned(16))) uint64_t s_key[GRAFT_MAX_CAND];
   __shared__ int s_par[GRAFT_MAX_CAND];
   __shared__ int s_ctok[GRAFT_MAX_CAND];
   __shared__ int s_idx[GRAFT_MAX_CAND];  // flattened index or -1
   __shared__ int s_wtot[kPasses * kWavesBT];
+  __shared__ uint64_t s_m1[4][64], s_m2[2][64], s_m3[64];  // merge partners, one buffer per round
+  __shared__ uint64_t s_thr;                                // smallest key kept
   __shared__ int s_np[GRAFT_MAX_NODES];
   __shared__ int s_nt[GRAFT_MAX_NODES];
   __shared__ int s_nsrc[GRAFT_MAX_NODES];
@@ -84,11 +172,14 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
   }
 
   // Stage everything in one round of loads.  Ranking key of candidate c >= 1:
-  // (order(score) << 11) | (2047 - c), so "o ranks before c" (higher score,
-  // ties to the lower index) is exactly key_o > key_c; the root's slot and
-  // the padding hold key 0, below every real key.
-  const int Cp = (C + 1) & ~1;
-  for (int c = tid; c < Cp; c += kThreads) {
+  // 2^43 | (order(score) << 11) | (2047 - c), so "o ranks before c" (higher
+  // score, ties to the lower index) is exactly key_o > key_c; the root and
+  // the padding hold key 0, below every real key.  Thread tid holds the key
+  // of candidate p * 512 + tid, so wavefront w of pass p holds block 8p + w.
+  uint64_t kreg[kPasses];
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int c = pass * kThreads + tid;
     uint64_t key = 0;
     if (c < C) {
       const float sc = cand_score[c0 + c];
@@ -100,47 +191,59 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
       s_score[c] = sc;
       s_par[c] = p;
       s_ctok[c] = t;
-      if (c > 0) key = (static_cast<uint64_t>(graft::float_order(sc)) << 11) | static_cast<uint64_t>(2047 - c);
+      if (c > 0)
+        key = (1ull << 43) | (static_cast<uint64_t>(graft::float_order(sc)) << 11) |
+              static_cast<uint64_t>(2047 - c);
     }
-    s_key[c] = key;
+    kreg[pass] = key;
   }
   for (int r = tid; r < R && r < GRAFT_MAX_NODES; r += kThreads) {
     s_rpar[r] = ret_parent[ro + r];
     s_rtok[r] = ret_token[ro + r];
   }
-  __syncthreads();
-
-  // keep the root and every candidate with fewer than bud-1 better others;
-  // one candidate per thread, one 64-bit compare per (candidate, other) pair
-  // on broadcast LDS reads; a wavefront stops once each of its candidates
-  // already has bud-1 better ones
-  const uint64_t need = static_cast<uint64_t>(bud - 1);
-  const ulonglong2 *kv = reinterpret_cast<const ulonglong2 *>(s_key);
-  for (int pass = 0; pass < kPasses; ++pass) {
-    if (pass * kThreads >= C) break;  // uniform
-    const int c = pass * kThreads + tid;
-    const bool live = c < C;
-    const uint64_t kc = live ? s_key[c] : ~0ull;  // padding lanes count nothing
-    uint64_t cnt = 0;
-    for (int o2 = 0; o2 < Cp / 2; o2 += 8) {
+  // Keep the root and the bud-1 best other candidates.  Each wavefront sorts
+  // its 64-key blocks in registers and folds them into the sorted 64 largest
+  // of its keys; three rounds of pairwise merges across wavefronts leave the
+  // 64 largest keys of the request in wavefront 0, where entry bud-2 is the
+  // smallest key kept.  Merge partners are sorted in opposite directions.
+  const int NB = (C + 63) / 64;
+  const bool dir0 = (wave & 1) == 0;
+  uint64_t top = wave_sort(kreg[0], lane64, dir0);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const ulonglong2 q = kv[min(o2 + u, Cp / 2 - 1)];
-        const uint64_t w = o2 + u < Cp / 2 ? 1ull : 0ull;
-        cnt += (q.x > kc ? w : 0ull) + (q.y > kc ? w : 0ull);
-      }
-      // every live candidate of this wavefront already excluded (the root
-      // stays in regardless)
-      if (__builtin_amdgcn_ballot_w64(live && c > 0 && cnt < need) == 0) break;
+  for (int pass = 1; pass < kPasses; ++pass)
+    if (pass * kWavesBT < NB)  // uniform
+      top = top64_merge(top, wave_sort(kreg[pass], lane64, !dir0), lane64, dir0);
+  if (wave & 1) s_m1[wave >> 1][lane64] = top;
+  __syncthreads();
+  if (!(wave & 1)) top = top64_merge(top, s_m1[wave >> 1][lane64], lane64, ((wave >> 1) & 1) == 0);
+  if ((wave & 3) == 2) s_m2[wave >> 2][lane64] = top;
+  __syncthreads();
+  if ((wave & 3) == 0) top = top64_merge(top, s_m2[wave >> 2][lane64], lane64, ((wave >> 2) & 1) == 0);
+  if (wave == 4) s_m3[lane64] = top;
+  __syncthreads();
+  const int need = bud - 1;
+  if (wave == 0) {
+    top = top64_merge(top, s_m3[lane64], lane64, true);
+    // need > 64 keeps the 64 largest, already more than a request can hold
+    const int at = need <= 0 ? 0 : (need < 64 ? need - 1 : 63);
+    if (lane64 == at) s_thr = need <= 0 ? ~0ull : top;
+  }
+  __syncthreads();
+  const uint64_t thr = s_thr;
+  // exclusive prefix of the keep flags: bit count below this lane within the
+  // wavefront, then the totals of the earlier wavefronts
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    if (pass * kThreads < C) {  // uniform
+      const int c = pass * kThreads + tid;
+      const bool live = c < C;
+      const bool keep = live && (c == 0 || kreg[pass] >= thr);
+      const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
+      const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+      if (lane64 == 0) s_wtot[pass * kWavesBT + wave] = __popcll(m);
+      if (live) s_idx[c] = keep ? below : -1;
     }
-    const bool keep = live && (c == 0 || cnt < need);
-    // exclusive prefix of the keep flags: bit count below this lane within
-    // the wavefront, then the totals of the earlier wavefronts
-    const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
-    const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-    if (lane64 == 0) s_wtot[pass * kWavesBT + wave] = __popcll(m);
-    if (live) s_idx[c] = keep ? below : -1;
   }
   __syncthreads();
   int nd = 0;
@@ -221,19 +324,26 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     int srcv = valid ? s_nsrc[lane] : -1;
 
     if (mode == GRAFT_TREE_STATIC_REPLACE) {
-      const bool low = valid && s_low[lane];
+      // j = index of this node among the low-confidence children of its
+      // parent, counted in flattened order
+      const int lowpar = (valid && s_low[lane]) ? par : -2;
       int j = 0;
-      for (int o = 1; o < lane; ++o) j += (s_low[o] && s_np[o] == par) ? 1 : 0;
-      int maxd = dep;
-      for (int off = 32; off > 0; off >>= 1) {
-        int v = __shfl_xor(maxd, off);
-        maxd = v > maxd ? v : maxd;
+      for (int o = 1; o < n; ++o) {
+        const int v = __builtin_amdgcn_readlane(lowpar, o);
+        j += (o < lane && v == par) ? 1 : 0;
       }
-      for (int level = 1; level <= maxd; ++level) {
-        int ptok = __shfl(tok, par >= 0 ? par : lane);
-        if (low && dep == level && j < k) {
+      // A node is replaced once its parent's token is final; only chains of
+      // replaced nodes need further rounds.  Parents precede children, so the
+      // first pending node is always ready and the loop ends.
+      bool pending = lowpar >= 0 && j < k;
+      for (int round = 0; round < GRAFT_MAX_NODES; ++round) {
+        if (__builtin_amdgcn_ballot_w64(pending) == 0) break;
+        const int from = par >= 0 ? par : lane;
+        const int ptok = __shfl(tok, from);
+        const bool ppend = __shfl(static_cast<int>(pending), from) != 0;
+        if (pending && !ppend) {
           if (ptok >= 0 && ptok < V) {
-            int t2 = table[static_cast<size_t>(ptok) * k + j];
+            const int t2 = table[static_cast<size_t>(ptok) * k + j];
             if (t2 >= 0 && t2 < V) {
               tok = t2;
               srcv = GRAFT_SRC_REPLACED;
@@ -243,6 +353,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
           } else {
             graft::raise_flag(err, GRAFT_ERR_TOKEN);
           }
+          pending = false;
         }
       }
     }

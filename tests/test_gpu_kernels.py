@@ -384,6 +384,36 @@ def test_build_ragged_batch_matches_oracle(api):
         assert np.array_equal(got[key], exp[key]), key
 
 
+def _tied_tree(r, C, V):
+    """Random tree of C candidates (parents precede children) whose scores are
+    powers of two, non-increasing along parent links: many exact ties, and
+    every top set under the (score, lower index) order is closed."""
+    par = np.full(C, -1, np.int32)
+    sc = np.ones(C, np.float32)
+    for c in range(1, C):
+        par[c] = r.integers(0, c)
+        sc[c] = sc[par[c]] * np.float32(r.choice([1.0, 0.5, 0.25]))
+    return par, r.integers(0, V, C).astype(np.int32), sc
+
+
+@pytest.mark.parametrize("sizes", [(1, 2, 64, 65, 128), (600, 1100, 2048)])
+def test_build_many_candidates_with_ties_matches_oracle(api, sizes):
+    r = W.rng(91, f"ties{len(sizes)}")
+    V = 5000
+    cands = [_tied_tree(r, C, V) for C in sizes]
+    budgets = [min(C, b) for C, b in zip(sizes, (64, 63, 60, 40, 8))]
+    ctx = [int(r.integers(0, 9000)) for _ in sizes]
+    caps = [b + 1 for b in budgets]
+    got, row_off, err = _build_gpu(api, 0, cands, budgets, None, ctx, caps, V=V)
+    assert err == 0
+    exp = OTree.build_batch(np.concatenate([c[0] for c in cands]), np.concatenate([c[1] for c in cands]),
+                            np.concatenate([c[2] for c in cands]),
+                            np.concatenate([[0], np.cumsum(sizes)]), budgets,
+                            np.zeros(0), np.zeros(0), np.zeros(len(sizes) + 1, np.int32), ctx, V, row_off)
+    for key in ("n", "parent", "token", "depth", "pos", "mask", "src"):
+        assert np.array_equal(got[key], exp[key]), key
+
+
 def test_build_chain_of_64_and_capacity_overflow(api):
     C = 64
     chain = (np.arange(-1, C - 1, dtype=np.int32), np.arange(C, dtype=np.int32),
