@@ -8,11 +8,13 @@
 //
 // One workgroup does both parts.  The update list is small (at most a few
 // thousand rows: the nodes of one round's trees), so the kernel is bound by
-// latency, not bandwidth.  Same-token conflicts are resolved with an LDS
-// hash map token -> largest row index; the winning rows are copied into
-// the table.  Retrieval then reads a row from the update list when its
-// token was just updated and from the table otherwise, so it never reads
-// memory this launch writes.
+// latency, not bandwidth: every global input is read in one round of loads,
+// and template rows resolve in rounds, one per level, each a single
+// dependent table read.  Same-token conflicts are resolved with an LDS hash
+// map token -> largest row index; the winning rows are copied into the
+// table.  Retrieval reads a row from the update list when its token was
+// just updated and from the table otherwise, so it never reads memory this
+// launch writes.
 #include "common.h"
 
 namespace {
@@ -58,6 +60,36 @@ __device__ int owner(const int *off, int nb, int r) {
   return lo;
 }
 
+// Token at rank `rank` of src's successor row: from the update list when src
+// was just updated (its winning row w), else from the table.  The table read
+// is issued before the hash probe so the two latencies overlap; a stale row
+// of an updated token is read and dropped.  Flags and returns -1 on a bad
+// rank, source or entry (a parent without a token, src == -1, below the
+// root, is not flagged again).
+__device__ inline int lookup(const int32_t *table, const int32_t *upd_topk, const int *s_key, const int *s_val,
+                             int V, int k, int src, int rank, bool below_root, int32_t *err) {
+  if (rank < 0 || rank >= k) {
+    graft::raise_flag(err, GRAFT_ERR_RANK);
+    return -1;
+  }
+  if (src < 0 || src >= V) {
+    if (!below_root || src != -1) graft::raise_flag(err, GRAFT_ERR_TOKEN);  // bad root or parent token
+    return -1;
+  }
+  const int tv = table[static_cast<size_t>(src) * k + rank];
+  const int w = hash_find(s_key, s_val, src);
+  const int tok = w >= 0 ? upd_topk[static_cast<size_t>(w) * k + rank] : tv;
+  if (tok < 0 || tok >= V) {
+    graft::raise_flag(err, GRAFT_ERR_TOKEN);
+    return -1;
+  }
+  return tok;
+}
+
+constexpr int kUpdPer = GRAFT_MAX_UPDATE_ROWS / kThreads;     // update rows per thread
+constexpr int kTmplPer = GRAFT_MAX_TEMPLATE_ROWS / kThreads;  // template rows per thread
+constexpr int kElemRegs = 8;  // update-list entries per thread held in registers (8192 in all)
+constexpr int kMaxDepth = 127;  // deepest template level expanded
 
 __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
     int32_t *__restrict__ table, int V, int k, int B_upd, const int32_t *__restrict__ upd_n,
@@ -68,25 +100,25 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
     int32_t *__restrict__ err) {
   __shared__ int s_key[kSlots];
   __shared__ int s_val[kSlots];
+  __shared__ int s_utok[GRAFT_MAX_UPDATE_ROWS];             // token of a live, valid update row, else -1
+  __shared__ unsigned char s_rowbad[GRAFT_MAX_UPDATE_ROWS];  // an id of the row is outside [0, V)
   __shared__ int s_tok[GRAFT_MAX_TEMPLATE_ROWS];
-  __shared__ int s_tp[GRAFT_MAX_TEMPLATE_ROWS];    // template parents
-  __shared__ int s_own[GRAFT_MAX_TEMPLATE_ROWS];   // owning request of each template row
-  __shared__ int s_utok[GRAFT_MAX_UPDATE_ROWS];    // token of a valid update row, else -1
-  __shared__ signed char s_rank[GRAFT_MAX_TEMPLATE_ROWS];
-  __shared__ signed char s_depth[GRAFT_MAX_TEMPLATE_ROWS];
+  __shared__ short s_round[GRAFT_MAX_TEMPLATE_ROWS];         // round a row was resolved in; -1 pending
+  __shared__ signed char s_bad[GRAFT_MAX_TEMPLATE_ROWS];     // broken parent chain
   __shared__ int s_toff[GRAFT_MAX_BATCH + 1];
   __shared__ int s_root[GRAFT_MAX_BATCH];
   __shared__ int s_uoff[GRAFT_MAX_BATCH + 1];
   __shared__ int s_un[GRAFT_MAX_BATCH];
-  __shared__ int s_maxdepth;
+  __shared__ int s_straddle;  // a request's template rows span two wavefronts
   const int tid = threadIdx.x;
+  const int n_elem = upd_rows * k;
 
-  // ---- one round of loads: offsets, roots, template structure
+  // ---- one round of coalesced loads: offsets, roots, the update list entry
+  // by entry, update tokens, template structure
   for (int h = tid; h < kSlots; h += kThreads) {
     s_key[h] = -1;
     s_val[h] = -1;
   }
-  if (tid == 0) s_maxdepth = 0;
   for (int b = tid; b <= B; b += kThreads) {
     s_toff[b] = toff[b];
     if (b < B) s_root[b] = root_token[b];
@@ -95,104 +127,161 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
     s_uoff[b] = upd_row_off[b];
     if (b < B_upd) s_un[b] = upd_n[b];
   }
-  for (int t = tid; t < tmpl_rows; t += kThreads) {
-    s_tp[t] = tparent[t];
-    s_rank[t] = static_cast<signed char>(min(max(trank[t], -1), 127));
+  if (tid == 0) s_straddle = tmpl_rows > kThreads ? 1 : 0;
+  int ev[kElemRegs];
+#pragma unroll
+  for (int q = 0; q < kElemRegs; ++q) {
+    const int e = q * kThreads + tid;
+    ev[q] = e < n_elem ? upd_topk[e] : 0;
+  }
+  int utok[kUpdPer];
+#pragma unroll
+  for (int u = 0; u < kUpdPer; ++u) {
+    const int r = u * kThreads + tid;
+    utok[u] = r < upd_rows ? upd_token[r] : -1;
+    if (r < upd_rows) s_rowbad[r] = 0;
+  }
+  int tpar[kTmplPer], trk[kTmplPer];
+#pragma unroll
+  for (int i = 0; i < kTmplPer; ++i) {
+    const int t = i * kThreads + tid;
+    tpar[i] = t < tmpl_rows ? tparent[t] : -1;
+    trk[i] = t < tmpl_rows ? trank[t] : -1;
   }
   __syncthreads();
-  for (int t = tid; t < tmpl_rows; t += kThreads) s_own[t] = owner(s_toff, B, t);
+
+  // ---- ids outside the vocabulary mark their row; request capacities;
+  // template rows: owner, and the link to a request-local parent, which must
+  // precede its child
+#pragma unroll
+  for (int q = 0; q < kElemRegs; ++q) {
+    const int e = q * kThreads + tid;
+    if (e < n_elem && (ev[q] < 0 || ev[q] >= V)) s_rowbad[e / k] = 1;
+  }
+  for (int e = kElemRegs * kThreads + tid; e < n_elem; e += kThreads) {
+    const int v = upd_topk[e];
+    if (v < 0 || v >= V) s_rowbad[e / k] = 1;
+  }
   for (int b = tid; b < B_upd; b += kThreads) {
     const int cap = s_uoff[b + 1] - s_uoff[b];
     const int nb = s_un[b];
     if (nb < 0 || nb > cap) graft::raise_flag(err, GRAFT_ERR_CAPACITY);
   }
+  int town[kTmplPer], tbase[kTmplPer];
+  unsigned pend = 0;
+#pragma unroll
+  for (int i = 0; i < kTmplPer; ++i) {
+    const int t = i * kThreads + tid;
+    town[i] = 0;
+    tbase[i] = 0;
+    if (t < tmpl_rows) {
+      town[i] = owner(s_toff, B, t);
+      tbase[i] = s_toff[town[i]];
+      const bool link_ok = tpar[i] < t - tbase[i];
+      if (!link_ok) graft::raise_flag(err, GRAFT_ERR_PARENT);
+      s_round[t] = link_ok ? -1 : 0;
+      s_bad[t] = link_ok ? 0 : 1;
+      if (link_ok) pend |= 1u << i;
+      if ((tbase[i] >> 6) != (t >> 6)) s_straddle = 1;
+    }
+  }
+  __syncthreads();
 
-  // ---- update rows: validity (verified node, token and ids in range);
-  // last writer wins: keep the largest row index per token
-  for (int r = tid; r < upd_rows; r += kThreads) {
-    const int b = owner(s_uoff, B_upd, r);
-    const int i = r - s_uoff[b];
-    const int nb = s_un[b];
+  // ---- update rows of verified nodes with valid ids; last writer wins: keep
+  // the largest row index per token
+#pragma unroll
+  for (int u = 0; u < kUpdPer; ++u) {
+    const int r = u * kThreads + tid;
+    if (r < upd_rows) {
+      const int b = owner(s_uoff, B_upd, r);
+      const bool live = r - s_uoff[b] < s_un[b] && r < s_uoff[b + 1];  // not a padding row
+      int t = -1;
+      if (live) {
+        if (utok[u] >= 0 && utok[u] < V && !s_rowbad[r]) t = utok[u];
+        else graft::raise_flag(err, GRAFT_ERR_TOKEN);
+      }
+      s_utok[r] = t;
+      if (t >= 0) hash_insert(s_key, s_val, t, r);
+    }
+  }
+  __syncthreads();
+
+  // ---- expand the templates: a row is resolved in the round after its
+  // parent, so round d resolves depth d.  When every request's rows sit in
+  // one wavefront (at most 1024 rows), each wavefront runs its own rounds
+  // and takes parent tokens by lane shuffle; otherwise parents are read
+  // from LDS between workgroup barriers.
+  if (!s_straddle) {
+    const int lane = tid & 63;
+    const int p = tpar[0];
+    const int pl = p >= 0 ? ((tbase[0] + p) & 63) : lane;  // parent's lane
+    bool pending = pend & 1u;
+    bool bad = tid < tmpl_rows && !pending;  // broken parent link
     int tok = -1;
-    if (i < nb && r < s_uoff[b + 1]) {  // not a padding row
-      const int t = upd_token[r];
-      bool ok = t >= 0 && t < V;
-      for (int j = 0; j < k; ++j) {
-        const int v = upd_topk[static_cast<size_t>(r) * k + j];
-        ok = ok && v >= 0 && v < V;
-      }
-      if (!ok) graft::raise_flag(err, GRAFT_ERR_TOKEN);
-      else tok = t;
-    }
-    s_utok[r] = tok;
-    if (tok >= 0) hash_insert(s_key, s_val, tok, r);
-  }
-  __syncthreads();
-
-  // ---- template depths (request-local parents must precede their child)
-  for (int t = tid; t < tmpl_rows; t += kThreads) {
-    const int base = s_toff[s_own[t]];
-    int cur = t - base;
-    int d = 1;
-    bool ok = true;
-    while (true) {
-      const int p = s_tp[base + cur];
-      if (p < 0) break;
-      if (p >= cur) {
-        ok = false;
-        break;
-      }
-      cur = p;
-      ++d;
-    }
-    if (!ok || d > 127) {
-      graft::raise_flag(err, GRAFT_ERR_PARENT);
-      s_depth[t] = -1;
-    } else {
-      s_depth[t] = static_cast<signed char>(d);
-      atomicMax(&s_maxdepth, d);
-    }
-  }
-  __syncthreads();
-
-  // ---- expand the templates level by level; a just-updated token's row is
-  // read from the update list, any other from the table (never memory this
-  // launch writes)
-  const int maxd = s_maxdepth;
-  for (int level = 1; level <= maxd; ++level) {
-    for (int t = tid; t < tmpl_rows; t += kThreads) {
-      if (s_depth[t] != level) continue;
-      const int b = s_own[t];
-      const int base = s_toff[b];
-      const int p = s_tp[t];
-      const int src = p < 0 ? s_root[b] : s_tok[base + p];
-      const int rank = s_rank[t];
-      int tok = -1;
-      if (rank < 0 || rank >= k) {
-        graft::raise_flag(err, GRAFT_ERR_RANK);
-      } else if (src >= 0 && src < V) {
-        const int w = hash_find(s_key, s_val, src);
-        tok = w >= 0 ? upd_topk[static_cast<size_t>(w) * k + rank] : table[static_cast<size_t>(src) * k + rank];
-        if (tok < 0 || tok >= V) {
-          graft::raise_flag(err, GRAFT_ERR_TOKEN);
-          tok = -1;
+    for (int round = 1; round <= kMaxDepth; ++round) {
+      if (__builtin_amdgcn_ballot_w64(pending) == 0) break;
+      const int ptok = __shfl(tok, pl);
+      const int pst = __shfl((pending ? 1 : 0) | (bad ? 2 : 0), pl);
+      if (pending && (p < 0 || !(pst & 1))) {
+        if (p >= 0 && (pst & 2)) {
+          graft::raise_flag(err, GRAFT_ERR_PARENT);
+          bad = true;
+        } else {
+          tok = lookup(table, upd_topk, s_key, s_val, V, k, p < 0 ? s_root[town[0]] : ptok, trk[0], p >= 0, err);
         }
-      } else if (p < 0 || src != -1) {
-        graft::raise_flag(err, GRAFT_ERR_TOKEN);  // bad root (or bad parent token)
+        pending = false;
       }
-      s_tok[t] = tok;
     }
-    __syncthreads();
+    if (pending) graft::raise_flag(err, GRAFT_ERR_PARENT);  // deeper than kMaxDepth levels
+    if (tid < tmpl_rows) ret_token[tid] = (!pending && !bad) ? tok : -1;
+  } else {
+    for (int round = 1; round <= kMaxDepth; ++round) {
+#pragma unroll
+      for (int i = 0; i < kTmplPer; ++i) {
+        if (!(pend & (1u << i))) continue;
+        const int t = i * kThreads + tid;
+        const int p = tpar[i];
+        const int pr = p < 0 ? 0 : s_round[tbase[i] + p];
+        if (p >= 0 && (pr < 0 || pr >= round)) continue;  // parent not resolved before this round
+        const bool bad = p >= 0 && s_bad[tbase[i] + p];
+        int tok = -1;
+        if (bad) {
+          graft::raise_flag(err, GRAFT_ERR_PARENT);
+        } else {
+          const int src = p < 0 ? s_root[town[i]] : s_tok[tbase[i] + p];
+          tok = lookup(table, upd_topk, s_key, s_val, V, k, src, trk[i], p >= 0, err);
+        }
+        s_tok[t] = tok;
+        s_bad[t] = bad ? 1 : 0;
+        s_round[t] = static_cast<short>(round);
+        pend &= ~(1u << i);
+      }
+      if (!__syncthreads_or(pend != 0)) break;
+    }
+    if (pend) graft::raise_flag(err, GRAFT_ERR_PARENT);  // deeper than kMaxDepth levels
+#pragma unroll
+    for (int i = 0; i < kTmplPer; ++i) {
+      const int t = i * kThreads + tid;
+      if (t < tmpl_rows)
+        ret_token[t] = (!(pend & (1u << i)) && !s_bad[t] && s_round[t] > 0) ? s_tok[t] : -1;
+    }
   }
-  for (int t = tid; t < tmpl_rows; t += kThreads) ret_token[t] = s_depth[t] > 0 ? s_tok[t] : -1;
 
-  // ---- copy the winning rows into the table (rows read above come from the
-  // update list for these tokens, so the order does not matter)
-  for (int r = tid; r < upd_rows; r += kThreads) {
+  // ---- copy the winning rows into the table, entry by entry (retrieval above
+  // read these tokens' rows from the update list)
+#pragma unroll
+  for (int q = 0; q < kElemRegs; ++q) {
+    const int e = q * kThreads + tid;
+    if (e < n_elem) {
+      const int r = e / k;
+      const int t = s_utok[r];
+      if (t >= 0 && hash_find(s_key, s_val, t) == r) table[static_cast<size_t>(t) * k + (e - r * k)] = ev[q];
+    }
+  }
+  for (int e = kElemRegs * kThreads + tid; e < n_elem; e += kThreads) {
+    const int r = e / k;
     const int t = s_utok[r];
-    if (t < 0 || hash_find(s_key, s_val, t) != r) continue;
-    for (int j = 0; j < k; ++j)
-      table[static_cast<size_t>(t) * k + j] = upd_topk[static_cast<size_t>(r) * k + j];
+    if (t >= 0 && hash_find(s_key, s_val, t) == r) table[static_cast<size_t>(t) * k + (e - r * k)] = upd_topk[e];
   }
 }
 

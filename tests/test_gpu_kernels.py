@@ -327,6 +327,80 @@ def test_table_invalid_rows_are_flagged_and_skipped(api):
     assert got_t[5].tolist() == [0, 1, 2, 3]  # skipped
 
 
+def test_table_template_edge_cases_and_4096_rows(api):
+    """Templates deeper than 127 levels, a parent link that does not precede
+    its child and a rank outside the table width are flagged and give -1 for
+    the affected rows only; the other requests of the batch (4096 template
+    rows in all) match the oracle."""
+    r = np.random.default_rng(2024)
+    V, k = 300, 8
+    table = np.stack([r.choice(V, k, replace=False) for _ in range(V)]).astype(np.int32)
+    n, row_off = np.array([0], np.int32), np.array([0, 1], np.int32)  # one padding update row
+    token, topk = np.array([5], np.int32), np.zeros((1, k), np.int32)
+    chain = (list(range(-1, 129)), [int(x) for x in r.integers(0, k, 130)])        # depth 130
+    badlink = ([-1, 0, 1, 3, 3, -1], [1, 2, 3, 4, 5, 6])                         # row 3 -> 3
+    badrank = ([-1, 0, 1, -1], [0, k, 0, 2])                                       # row 1 rank k
+    specials = [chain, badlink, badrank]
+    valid = []
+    used = sum(len(x[0]) for x in specials)
+    while used < 4096:
+        R = min(int(r.integers(1, 64)), 4096 - used)
+        tp, tr, _ = otemplate(R, k, 8)
+        valid.append((list(tp), list(tr)))
+        used += R
+    tmpl = specials + valid
+    roots = r.integers(0, V, len(tmpl)).astype(np.int32)
+    tps = np.concatenate([np.array(x[0], np.int32) for x in tmpl])
+    trs = np.concatenate([np.array(x[1], np.int32) for x in tmpl])
+    toff = np.concatenate([[0], np.cumsum([len(x[0]) for x in tmpl])]).astype(np.int32)
+    assert toff[-1] == 4096
+    got_t, got_r, err = _table_gpu(api, table, n, row_off, token, topk, roots, tps, trs, toff)
+    assert err == ERR_PARENT | ERR_RANK
+    assert np.array_equal(got_t, table)
+    seg = [got_r[toff[i]:toff[i + 1]].tolist() for i in range(len(tmpl))]
+    exp_chain = OTab.retrieve(table, int(roots[0]), chain[0], chain[1])
+    assert seg[0] == exp_chain[:127] + [-1] * 3
+    head = OTab.retrieve(table, int(roots[1]), [-1, 0, 1], [1, 2, 3])
+    assert seg[1] == head + [-1, -1, int(table[roots[1], 6])]
+    assert seg[2] == [int(table[roots[2], 0]), -1, -1, int(table[roots[2], 2])]
+    for i in range(3, len(tmpl)):
+        assert seg[i] == OTab.retrieve(table, int(roots[i]), tmpl[i][0], tmpl[i][1]), i
+
+
+def test_table_wave_local_templates_match_oracle(api):
+    """Batches whose template rows never cross a 64-row boundary (each
+    request's rows inside one wavefront): a broken parent link, a bad rank
+    and the rows after them, a just-updated root, and full 64-row
+    templates."""
+    r = np.random.default_rng(99)
+    V, k = 400, 8
+    table = np.stack([r.choice(V, k, replace=False) for _ in range(V)]).astype(np.int32)
+    # update rows: tokens 7 and 11 (11 twice: the later row wins)
+    token = np.array([7, 11, 11], np.int32)
+    topk = np.stack([r.choice(V, k, replace=False) for _ in range(3)]).astype(np.int32)
+    n, row_off = np.array([3], np.int32), np.array([0, 3], np.int32)
+    badlink = ([-1, 0, 1, 3, 3, -1], [1, 2, 3, 4, 5, 6])
+    badrank = ([-1, 0, 1, -1], [0, k, 0, 2])
+    tp54, tr54, _ = otemplate(54, k, 8)   # rows 10..63: ends on the wavefront boundary
+    tp64, tr64, _ = otemplate(64, k, 8)   # rows 64..127: a whole wavefront
+    tmpl = [badlink, badrank, (list(tp54), list(tr54)), (list(tp64), list(tr64))]
+    roots = np.array([3, 11, 7, 250], np.int32)
+    tps = np.concatenate([np.array(x[0], np.int32) for x in tmpl])
+    trs = np.concatenate([np.array(x[1], np.int32) for x in tmpl])
+    toff = np.concatenate([[0], np.cumsum([len(x[0]) for x in tmpl])]).astype(np.int32)
+    assert toff.tolist() == [0, 6, 10, 64, 128]
+    got_t, got_r, err = _table_gpu(api, table, n, row_off, token, topk, roots, tps, trs, toff)
+    assert err == ERR_PARENT | ERR_RANK
+    exp_t = OTab.update(table, n, row_off, token, topk)
+    assert np.array_equal(got_t, exp_t)
+    seg = [got_r[toff[i]:toff[i + 1]].tolist() for i in range(len(tmpl))]
+    head = OTab.retrieve(exp_t, 3, [-1, 0, 1], [1, 2, 3])
+    assert seg[0] == head + [-1, -1, int(exp_t[3, 6])]
+    assert seg[1] == [int(exp_t[11, 0]), -1, -1, int(exp_t[11, 2])]
+    assert seg[2] == OTab.retrieve(exp_t, 7, tmpl[2][0], tmpl[2][1])
+    assert seg[3] == OTab.retrieve(exp_t, 250, tmpl[3][0], tmpl[3][1])
+
+
 # ----------------------------------------------------------------------------- build tree
 
 def _build_gpu(api, mode, cands, budgets, rets, ctx, caps, table=None, V=1000, k=8, thresh=0.05):
