@@ -121,6 +121,7 @@ class VerifyRound:
         self.acc_path = z(B, 64)
         self.bonus = z(B)
         self.graph = None
+        self.graph_rounds = 0
 
     def set_hidden(self, hidden_bits):
         self.hidden = _bf16(hidden_bits.reshape(self.rows, self.wl.H), self.dev)
@@ -186,21 +187,27 @@ class VerifyRound:
                 e1.record()
                 events.setdefault(name, []).append((e0, e1))
 
-    def capture(self):
-        """Record one round as a HIP graph with the update pointers as they
-        stand (call chain_update() first for steady-state rounds: every round
-        then reads the previous round's outputs from the same buffers).
-        Nothing runs during capture; replay() issues one round.  The round
-        has no memset nodes and no host synchronisation, so it replays as
-        recorded."""
+    def capture(self, rounds: int = 1):
+        """Record `rounds` consecutive rounds as one HIP graph with the update
+        pointers as they stand (call chain_update() first for steady-state
+        rounds: every round then reads the previous round's outputs from the
+        same buffers, so rounds chain inside the graph as they do across
+        replays).  Nothing runs during capture; replay() issues the rounds.
+        The rounds have no memset nodes and no host synchronisation, so they
+        replay as recorded."""
+        if rounds < 1:
+            raise ValueError("rounds must be >= 1")
         g = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            self.run()
+            for _ in range(rounds):
+                self.run()
         self.graph = g
+        self.graph_rounds = rounds
         return g
 
     def replay(self):
+        """Issue the captured rounds (graph_rounds of them)."""
         self.graph.replay()
 
     def tree_host(self):

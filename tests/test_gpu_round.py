@@ -146,11 +146,12 @@ def test_end_to_end_argmax_where_margin_is_clear():
     say(f"[e2e] {int(clear.sum())} of {len(rows)} rows have a clear margin; all match")
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
-def test_graph_replay_matches_eager(cfg):
-    """A round captured as a HIP graph and replayed several times (with
-    unrelated eager work and synchronisations between replays) gives, round
-    after round, exactly what the same rounds give issued eagerly."""
+@pytest.mark.parametrize("cfg,per_graph", [(1, 1), (2, 1), (2, 3)])
+def test_graph_replay_matches_eager(cfg, per_graph):
+    """Rounds captured as a HIP graph (per_graph chained rounds in one graph)
+    and replayed several times, with unrelated eager work and
+    synchronisations between replays, give, replay after replay, exactly
+    what the same rounds give issued eagerly."""
     _need_gpu()
     from draft_tree_verification_parent_amd.verify_round import VerifyRound
 
@@ -162,11 +163,12 @@ def test_graph_replay_matches_eager(cfg):
         vr.set_hidden(hidden)
         vr.run()
         vr.chain_update()
-    graph.capture()
+    graph.capture(per_graph)
     outs = ("table", "ret_token", "n_out", "parent", "token", "depth", "pos", "mask", "src",
             "attn_out", "lse", "topk_id", "topk_val", "acc_len", "acc_path", "bonus", "err")
     for rnd in range(4):
-        eager.run()
+        for _ in range(per_graph):
+            eager.run()
         torch.cuda.synchronize()
         junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
         torch.cuda.synchronize()
@@ -185,5 +187,5 @@ def test_graph_replay_matches_eager(cfg):
                 a, b = a[: eager.tmpl_rows], b[: graph.tmpl_rows]
             elif name in ("attn_out", "lse"):
                 a, b = a[live], b[live]
-            assert torch.equal(a, b), f"round {rnd + 2}: {name} differs between replay and eager"
-    say(f"[graph] cfg {cfg}: 4 replays identical to eager rounds")
+            assert torch.equal(a, b), f"replay {rnd + 1}: {name} differs between replay and eager"
+    say(f"[graph] cfg {cfg}: 4 replays of {per_graph} round(s) identical to eager rounds")
