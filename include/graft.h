@@ -13,6 +13,10 @@
  *   graft_lmhead_topk            logits = hidden . W^T and per-row top-k
  *                                (weights packed once by graft_lmhead_pack)
  *   graft_accept                 deepest greedily accepted path + bonus token
+ *   graft_kv_compact             (round chaining) the accepted path's K/V
+ *                                moves to the front of the tree slots, the
+ *                                context advances, the bonus becomes the
+ *                                next root
  *
  * Conventions shared by every entry point
  *  - Pointers marked (device) are device memory owned by the caller; the
@@ -255,6 +259,36 @@ int graft_accept(int B, const int32_t *n, const int32_t *row_off,
                  const int32_t *parent, const int32_t *token, const int32_t *topk_id, int k,
                  int32_t *acc_len, int32_t *acc_path, int32_t *bonus, int32_t *err_flag,
                  graft_stream stream);
+
+/*
+ * KV compaction and round chaining (Graft page, section 2, third step: the
+ * flattened tree is verified in one pass and only the accepted output is
+ * kept; the next round drafts from the bonus token).  The tree's K/V sit
+ * at slots ctx .. ctx+n-1 in flattened order (the layout graft_tree_attention
+ * reads), so after acceptance the cache must hold, after the ctx context
+ * tokens, the accepted path root, p1, .., pa in order:
+ *   for every layer l < n_layers, KV head h < Hkv and t = 0 .. acc_len[b]:
+ *     slot ctx + t  <-  slot ctx + acc_path[b * 64 + t]   (K and V rows)
+ *   ctx_next[b]  = ctx_len[b] + acc_len[b] + 1
+ *   root_next[b] = bonus[b]
+ * Row (b, l, h, s) of kcache / vcache (device bf16, updated in place) starts
+ * at element l * layer_stride + kv_off[b] + h * kv_head_stride + s * d.
+ * ctx_len, acc_len, acc_path (graft_accept's layout), bonus, n (tree sizes):
+ * device int32.  ctx_next, root_next: device int32 [B], which must not alias
+ * ctx_len (every workgroup of a request reads it); chained rounds alternate
+ * two buffers.  Slots past ctx + acc_len are left as they are.  A request
+ * whose path is malformed (acc_len outside [0, 63], acc_path[0] != 0, not
+ * increasing, or a node >= n) flags ERR_PARENT, one whose tree does not fit
+ * (ctx + n > kv_head_stride / d) flags ERR_CAPACITY; neither moves any row,
+ * and both get ctx_next = ctx_len, root_next = -1.
+ * d in {64, 128}; n_layers >= 1; layer_stride >= B-wide cache extent when
+ * n_layers > 1 (not checked: the caller's layout).
+ */
+int graft_kv_compact(int B, int Hkv, int d, int n_layers, graft_bf16 *kcache, graft_bf16 *vcache,
+                     int64_t layer_stride, const int64_t *kv_off, int64_t kv_head_stride,
+                     const int32_t *ctx_len, const int32_t *n, const int32_t *acc_len,
+                     const int32_t *acc_path, const int32_t *bonus, int32_t *ctx_next,
+                     int32_t *root_next, int32_t *err_flag, graft_stream stream);
 
 /*
  * Host helper: the stage-adaptive retrieval template of R nodes (Graft

@@ -31,6 +31,7 @@ Modules:
   lmhead     -- logits = hidden . W^T
   topk       -- per-row top-k / argmax, ties to the lower id
   accept     -- greedy acceptance: deepest accepted node, path, bonus token
+  kv         -- KV compaction to the accepted path and round chaining
   round      -- the above composed into one round
 """
 
