@@ -29,6 +29,8 @@ SIGNATURES = {
     "graft_lmhead_pack_bytes": (c_size_t, [c_int, c_int]),
     "graft_lmhead_pack": (c_int, [c_int, c_int, P, P, P]),
     "graft_accept": (c_int, [c_int, P, P, P, P, P, c_int, P, P, P, P, P]),
+    "graft_kv_compact": (c_int, [c_int, c_int, c_int, c_int, P, P, c_int64, P, c_int64, P, P, P, P, P, P, P, P,
+                                 P]),
     "graft_make_template": (c_int, [c_int, c_int, c_int, P, P]),
     "graft_stage_budget": (c_int, [c_int, P, P]),
 }

@@ -121,6 +121,20 @@ def graft_accept(n, row_off, parent, token, topk_id, k, acc_len, acc_path, bonus
                 _p(bonus, "i32", "bonus"), _p(err, "i32", "err"), _s(stream))
 
 
+def graft_kv_compact(Hkv, d, kcache, vcache, kv_off, kv_head_stride, ctx_len, n, acc_len, acc_path, bonus,
+                     ctx_next, root_next, n_layers=1, layer_stride=0, err=None, stream=None):
+    """Moves each request's accepted path K/V to slots ctx..ctx+a (every
+    layer and KV head), writes ctx_next = ctx + a + 1 and root_next = bonus.
+    kcache / vcache: bf16 caches addressed as in graft_tree_attention, plus
+    `layer` * layer_stride elements."""
+    B = ctx_len.numel()
+    return call("graft_kv_compact", B, int(Hkv), int(d), int(n_layers), _p(kcache, "bf16", "kcache"),
+                _p(vcache, "bf16", "vcache"), int(layer_stride), _p(kv_off, "i64", "kv_off"), int(kv_head_stride),
+                _p(ctx_len, "i32", "ctx_len"), _p(n, "i32", "n"), _p(acc_len, "i32", "acc_len"),
+                _p(acc_path, "i32", "acc_path"), _p(bonus, "i32", "bonus"), _p(ctx_next, "i32", "ctx_next"),
+                _p(root_next, "i32", "root_next"), _p(err, "i32", "err"), _s(stream))
+
+
 def graft_make_template(R, k, dmax=8):
     """Host helper: (tmpl_parent, tmpl_rank) int32 numpy arrays of length R."""
     tp = np.zeros(max(R, 1), np.int32)

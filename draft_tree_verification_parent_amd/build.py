@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgraft.so")
 
 SOURCES = ["common.cpp", "template.cpp", "table.hip", "build_tree.hip", "accept.hip",
-           "topk.hip", "lmhead.hip", "attention.hip"]
+           "topk.hip", "lmhead.hip", "attention.hip", "kv_compact.hip"]
 ARCH = "gfx950"
 CXXFLAGS = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
             f"-I{INCLUDE}", f"-I{CSRC}"]

@@ -126,3 +126,23 @@ def test_workspace_sizes(native):
     # tiny single-split attention needs no workspace; long context does
     assert L.graft_tree_attention_workspace_bytes(1, 4, 2, 64, 100, 15) == 0
     assert L.graft_tree_attention_workspace_bytes(1, 32, 8, 128, 32768, 63) > 0
+
+
+def test_kv_compact_host_validation_launches_nothing(native):
+    L = native.lib()
+    E, U = native.GRAFT_EINVAL, native.GRAFT_EUNSUPPORTED
+    p = 1  # never dereferenced: every call below fails before a launch
+    args = lambda B=1, Hkv=8, d=128, nl=1, ls=0, hs=128 * 100, ctx=2, nxt=3: (  # noqa: E731
+        B, Hkv, d, nl, p, p, ls, p, hs, ctx, p, p, p, p, nxt, p, None, None)
+    assert L.graft_kv_compact(*args(B=0)) == 0                  # nothing to do
+    assert L.graft_kv_compact(*args(d=96)) == U                 # head dim not built
+    assert L.graft_kv_compact(*args(hs=100)) == E               # stride not a multiple of d
+    assert L.graft_kv_compact(*args(hs=0)) == E
+    assert L.graft_kv_compact(*args(nl=0)) == E
+    assert L.graft_kv_compact(*args(nl=2, ls=0)) == E           # layers without a layer stride
+    assert L.graft_kv_compact(*args(Hkv=0)) == E
+    assert L.graft_kv_compact(*args(B=-1)) == E
+    assert L.graft_kv_compact(*args(nxt=2)) == E                # ctx_next aliases ctx_len
+    a = list(args())
+    a[14] = None                                                 # ctx_next NULL
+    assert L.graft_kv_compact(*a) == E

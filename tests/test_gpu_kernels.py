@@ -5,6 +5,7 @@ import pytest
 
 from oracle import OracleError
 from oracle import accept as OAcc
+from oracle import kv as OKV
 from oracle import attention as OA
 from oracle import lmhead as OL
 from oracle import table as OTab
@@ -527,6 +528,72 @@ def test_build_static_replace_matches_oracle(api):
     for key in ("n", "parent", "token", "depth", "pos", "mask", "src"):
         assert np.array_equal(got[key], exp[key]), key
     assert (got["src"] == 3).sum() > 100
+
+
+# ----------------------------------------------------------------------------- KV compaction
+
+def _kv_case(r, d, L=2, Hkv=3, cap=160):
+    """Requests: ragged random paths, root only, the longest path (63), a
+    malformed path and a tree past the cache."""
+    specs = ["rand", "rand", "root", "max", "rand", "badpath", "overflow", "rand"]
+    B = len(specs)
+    ctx, n, lens, paths, bonus = [], [], [], [], []
+    for sp in specs:
+        nb = 64 if sp == "max" else int(r.integers(1, 65))
+        c = int(r.integers(0, cap - nb + 1))
+        if sp == "root":
+            path = [0]
+        elif sp == "max":
+            path = list(range(64))
+        else:
+            a = int(r.integers(0, min(nb, 64)))
+            path = [0] + sorted(int(x) for x in r.choice(np.arange(1, nb), a, replace=False)) if a else [0]
+        if sp == "badpath":
+            nb = max(nb, 4)
+            path = [0, 3, 2]
+        if sp == "overflow":
+            c = cap - nb + 1
+        ctx.append(c), n.append(nb), lens.append(len(path) - 1), paths.append(path)
+        bonus.append(int(r.integers(0, 1000)))
+    kc = r.integers(0, 65536, (L, B, Hkv, cap, d)).astype(np.uint16)
+    vc = r.integers(0, 65536, (L, B, Hkv, cap, d)).astype(np.uint16)
+    return specs, kc, vc, ctx, n, lens, paths, bonus
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_kv_compact_matches_oracle(api, d):
+    r = np.random.default_rng(400 + d)
+    L, Hkv, cap = 2, 3, 160
+    specs, kc, vc, ctx, n, lens, paths, bonus = _kv_case(r, d, L, Hkv, cap)
+    B = len(specs)
+    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)  # noqa: E731
+    kd, vd = to_dev(kc.copy()), to_dev(vc.copy())
+    kv_off = torch.from_numpy(np.arange(B, dtype=np.int64) * Hkv * cap * d).cuda()
+    pth = np.full((B, 64), -1, np.int32)
+    for b, pa in enumerate(paths):
+        pth[b, :len(pa)] = pa
+    ctx_next = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    root_next = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    err = err_buf()
+    ctx_d = dev_i32(ctx)
+    api.graft_kv_compact(Hkv, d, kd, vd, kv_off, cap * d, ctx_d, dev_i32(n), dev_i32(lens), dev_i32(pth),
+                         dev_i32(bonus), ctx_next, root_next, n_layers=L, layer_stride=B * Hkv * cap * d, err=err)
+    torch.cuda.synchronize()
+    assert err.item() == ERR_PARENT | ERR_CAPACITY
+    gk = kd.view(torch.int16).cpu().numpy().view(np.uint16)
+    gv = vd.view(torch.int16).cpu().numpy().view(np.uint16)
+    cn, rn = ctx_next.cpu().numpy(), root_next.cpu().numpy()
+    assert ctx_d.cpu().numpy().tolist() == ctx  # the input context is not touched
+    for b, sp in enumerate(specs):
+        if sp in ("badpath", "overflow"):  # flagged: nothing moves
+            assert np.array_equal(gk[:, b], kc[:, b]) and np.array_equal(gv[:, b], vc[:, b]), sp
+            assert cn[b] == ctx[b] and rn[b] == -1, sp
+            continue
+        k2, v2, c2, r2 = OKV.compact_batch(kc[:, b:b + 1], vc[:, b:b + 1], [ctx[b]], [n[b]], [lens[b]],
+                                           [paths[b]], [bonus[b]])
+        assert np.array_equal(gk[:, b], k2[:, 0]), (sp, b)
+        assert np.array_equal(gv[:, b], v2[:, 0]), (sp, b)
+        assert cn[b] == c2[0] and rn[b] == r2[0]
 
 
 # ----------------------------------------------------------------------------- attention
