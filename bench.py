@@ -231,6 +231,42 @@ def main():
                                               / MFMA_BF16_PEAK_TFS, 4)},
     }
 
+    # KV compaction (round chaining) on this round's accepted paths: the
+    # accepted rows move within the tree slots; the context is not advanced
+    # here (the next context goes to a scratch buffer), so every call moves
+    # the same rows.  Algorithmic bytes: each moved K and V row read once and
+    # written once.
+    from draft_tree_verification_parent_amd import api
+    ctx_s = torch.empty_like(vr.ctx_len)
+    root_s = torch.empty_like(vr.root_token)
+    acc_len_h = vr.acc_len.cpu().numpy()
+    acc_path_h = vr.acc_path.cpu().numpy()
+    moved = sum(int(np.sum(acc_path_h[b, 1:acc_len_h[b] + 1] != np.arange(1, acc_len_h[b] + 1)))
+                for b in range(ri.B))
+    kv_bytes = moved * wl.Hkv * wl.d * 2 * 2 * 2
+
+    def compact():
+        api.graft_kv_compact(wl.Hkv, wl.d, vr.kcache, vr.vcache, vr.kv_off, ri.kv_head_stride, vr.ctx_len,
+                             vr.n_out, vr.acc_len, vr.acc_path, vr.bonus, ctx_s, root_s, err=vr.err)
+    for _ in range(3):
+        compact()
+    torch.cuda.synchronize()
+    kv_graph = torch.cuda.CUDAGraph()  # `steps` calls in one graph: kernel time, not host launch time
+    with torch.cuda.graph(kv_graph):
+        for _ in range(args.steps):
+            compact()
+    kv_graph.replay()
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    kv_graph.replay()
+    c1.record()
+    torch.cuda.synchronize()
+    kv_us = c0.elapsed_time(c1) * 1e3 / args.steps
+    kernels["kv_compact"] = {"us": round(kv_us, 2), "rows_moved": moved, "bytes": kv_bytes,
+                             "hbm_frac": round(kv_bytes / (kv_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 6),
+                             "note": "round chaining step, timed on its own (not in the round)"}
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host (cpu_baseline)")

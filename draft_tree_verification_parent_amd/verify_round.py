@@ -12,7 +12,10 @@ section 6, second level):
                                     (logits never written) or, with
                                     fused=False, as two calls that
                                     materialise the logits;
-  5. graft_accept                -- deepest accepted path and bonus token.
+  5. graft_accept                -- deepest accepted path and bonus token;
+  6. graft_kv_compact            -- (chain=True) the accepted path's K/V to
+                                    the front of the tree slots, the context
+                                    advances, the bonus becomes the root.
 The next round's update reads this round's tree tokens and top-k ids.
 
 Device memory comes from torch; every computation runs in libgraft.
@@ -40,13 +43,17 @@ def _bf16(bits, dev):
 
 class VerifyRound:
     def __init__(self, ri, w_bits=None, device="cuda", dmax: int = 8, fused: bool = True,
-                 packed: bool = True):
+                 packed: bool = True, chain: bool = False):
         """fused: lm-head and top-k in one pass (logits never stored);
         packed: the lm-head weight is packed once here (when H % 128 == 0)
-        and the fused pass reads the packed copy."""
+        and the fused pass reads the packed copy;
+        chain: every round ends with KV compaction and the next round
+        starts from its context and root (the cache needs headroom: see
+        synth make_round_inputs(extra_slots=...))."""
         dev = torch.device(device)
         self.fused = fused
-        self.steps = STEPS_FUSED if fused else STEPS_SPLIT
+        self.chain = chain
+        self.steps = (STEPS_FUSED if fused else STEPS_SPLIT) + (("kv_compact",) if chain else ())
         wl = ri.wl
         self.ri, self.wl, self.dev = ri, wl, dev
         B, N, k, V = ri.B, ri.N, ri.k, ri.V
@@ -73,7 +80,9 @@ class VerifyRound:
         self.max_cand = int(np.max(np.diff(ri.cand_off)))
         self.budget = _i32(ri.budget, dev)
         self.ctx_len = _i32(ri.ctx_len, dev)
-        self.max_ctx = int(np.max(ri.ctx_len))
+        # chained rounds plan attention for the largest context the cache
+        # can still hold a tree after
+        self.max_ctx = int(ri.kv_cap - ri.N) if chain else int(np.max(ri.ctx_len))
         self.row_off = _i32(ri.row_off, dev)
         self.root_token = _i32(ri.root_token, dev)
         self.mode = TREE_STATIC_REPLACE if wl.static_replace else TREE_PRUNE
@@ -122,6 +131,13 @@ class VerifyRound:
         self.bonus = z(B)
         self.graph = None
         self.graph_rounds = 0
+        if chain:
+            # the next round's context and root are written to the other
+            # buffer of each pair (compaction reads the current one in every
+            # workgroup); the pairs swap after each round
+            self.ctx_alt = z(B)
+            self.root_alt = z(B)
+            self.cand_root_idx = torch.from_numpy(np.asarray(ri.cand_off[:-1], np.int64)).to(dev)
 
     def set_hidden(self, hidden_bits):
         self.hidden = _bf16(hidden_bits.reshape(self.rows, self.wl.H), self.dev)
@@ -168,6 +184,17 @@ class VerifyRound:
         api.graft_lmhead_topk(self.rows, self.wl.H, self.V, self.k, None, None, self.logits,
                               self.topk_id, self.topk_val, self.topk_ws)
 
+    def step_kv_compact(self):
+        wl = self.wl
+        api.graft_kv_compact(wl.Hkv, wl.d, self.kcache, self.vcache, self.kv_off, self.ri.kv_head_stride,
+                             self.ctx_len, self.n_out, self.acc_len, self.acc_path, self.bonus,
+                             self.ctx_alt, self.root_alt, err=self.err)
+        # drafter stand-in: the next round's candidates hang off the new root
+        self.cand_token.index_copy_(0, self.cand_root_idx, self.root_alt)
+        self.ctx_len, self.ctx_alt = self.ctx_alt, self.ctx_len
+        self.root_token, self.root_alt = self.root_alt, self.root_token
+        self.chain_update()
+
     def step_accept(self):
         api.graft_accept(self.n_out, self.row_off, self.parent, self.token, self.topk_id, self.k,
                          self.acc_len, self.acc_path, self.bonus, self.err)
@@ -197,6 +224,10 @@ class VerifyRound:
         replay as recorded."""
         if rounds < 1:
             raise ValueError("rounds must be >= 1")
+        if self.chain and rounds % 2:
+            # each chained round swaps the context / root buffers; an odd
+            # count would start every replay from the stale pair
+            raise ValueError("chained rounds are captured in even numbers")
         g = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
         with torch.cuda.graph(g):

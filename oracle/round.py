@@ -6,7 +6,8 @@ current token's retrieval tree is read from the updated table, the hybrid
 tree is built and flattened, the target verifies it (tree attention, then
 the lm-head), every position's top-k is taken, and the deepest greedily
 accepted path is kept.  The next round's update reads this round's tokens
-and top-k.
+and top-k; chaining (next_round_inputs) then compacts the accepted path's
+K/V, advances the context and makes the bonus token the next root.
 
 The inputs object only needs the attributes named below (numpy arrays);
 hidden states are passed in because the synthetic target model plants them
@@ -18,6 +19,7 @@ import numpy as np
 
 from . import accept as _accept
 from . import attention as _attention
+from . import kv as _kv
 from . import lmhead as _lmhead
 from . import table as _table
 from . import template as _template
@@ -74,3 +76,31 @@ def verify_stage(ri, tree, hidden_bits, w_bits, attention_nodes=None):
                                               tree["token"], ids[:, 0])
     return dict(attention=att, logits=logits, topk_id=ids, topk_val=vals,
                 acc_len=lens, acc_path=paths, bonus=bonus)
+
+
+def next_round_inputs(ri, ts, topk_id, acc_len, acc_path, bonus):
+    """The inputs of the round after `ri` (Graft page, section 2, third
+    step: only the accepted output is kept; the table update reads every
+    verified position): the updated table, this round's tree tokens and
+    top-k ids as the update list, the accepted path's K/V compacted to the
+    front of the tree slots, ctx + a + 1, and the bonus token as the root --
+    of retrieval and of the drafter stand-in's candidates alike (their
+    candidate 0).  Returns a new inputs object; `ri` is not modified."""
+    nxt = type(ri)(**dict(ri.__dict__))
+    tree = ts["tree"]
+    B = ri.B
+    kc, vc, ctx_next, root_next = _kv.compact_batch(ri.kcache[None], ri.vcache[None], ri.ctx_len, tree["n"],
+                                                    acc_len, acc_path, bonus)
+    nxt.kcache, nxt.vcache = kc[0], vc[0]
+    nxt.ctx_len = ctx_next.astype(np.int32)
+    nxt.root_token = root_next.astype(np.int32)
+    cand_token = np.array(ri.cand_token, np.int32).copy()
+    for b in range(B):
+        cand_token[int(ri.cand_off[b])] = int(bonus[b])
+    nxt.cand_token = cand_token
+    nxt.table = ts["table"]
+    nxt.prev_n = np.array(tree["n"], np.int32)
+    nxt.prev_row_off = np.array(ri.row_off, np.int32)
+    nxt.prev_token = np.array(tree["token"], np.int32)
+    nxt.prev_topk = np.array(topk_id, np.int32)
+    return nxt

@@ -265,7 +265,9 @@ def _normal_bf16(r: np.random.Generator, shape, std: float = 1.0) -> np.ndarray:
     return f32_to_bf16_bits(x)
 
 
-def make_round_inputs(wl: Workload, kv: bool = True) -> RoundInputs:
+def make_round_inputs(wl: Workload, kv: bool = True, extra_slots: int = 0) -> RoundInputs:
+    """extra_slots: cache slots per (request, KV head) beyond ctx_hi + N, for
+    chained rounds whose context grows."""
     cfg = wl.cfg
     B, N, k, V = wl.B, wl.n_nodes, wl.k, wl.V
     rc = rng(cfg, "ctx_len")
@@ -317,18 +319,18 @@ def make_round_inputs(wl: Workload, kv: bool = True) -> RoundInputs:
         scale=float(1.0 / np.sqrt(wl.d)),
     )
     if kv:
-        make_qkv(ri)
+        make_qkv(ri, extra_slots)
     return ri
 
 
-def make_qkv(ri: RoundInputs) -> None:
+def make_qkv(ri: RoundInputs, extra_slots: int = 0) -> None:
     """Q [B*N, Hq, d] and K/V caches laid out [B][Hkv][cap][d] with
-    cap = ctx_hi + N; request b's tree keys sit at slots ctx_b .. ctx_b+N-1.
-    Slots past ctx_b + N are zero."""
+    cap = ctx_hi + N + extra_slots; request b's tree keys sit at slots
+    ctx_b .. ctx_b+N-1.  Slots past ctx_b + N are zero."""
     wl = ri.wl
     cfg = wl.cfg
     B, N = ri.B, ri.N
-    cap = wl.ctx_hi + N
+    cap = wl.ctx_hi + N + extra_slots
     ri.kv_cap = cap
     ri.kv_head_stride = cap * wl.d
     ri.kv_off = (np.arange(B, dtype=np.int64) * wl.Hkv * cap * wl.d)

@@ -14,6 +14,7 @@ from oracle import attention as OA
 from oracle import lmhead as OL
 from oracle import round as OR
 from oracle import topk as OT
+from synth import workloads as W
 
 from _gpu_round import bf16_tensor_to_f64, run_gpu_round, say, within_tol
 
@@ -189,3 +190,99 @@ def test_graph_replay_matches_eager(cfg, per_graph):
                 a, b = a[live], b[live]
             assert torch.equal(a, b), f"replay {rnd + 1}: {name} differs between replay and eager"
     say(f"[graph] cfg {cfg}: 4 replays of {per_graph} round(s) identical to eager rounds")
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_chained_rounds_match_oracle(cfg):
+    """Three rounds chained on the GPU (KV compaction, context advance, bonus
+    token as the next root) against the oracle's chain, round by round: the
+    table, retrieval and tree bit-exact, attention on sampled nodes within
+    tolerance over the compacted cache, top-k and acceptance on the GPU's
+    fp32 logits, and the whole K/V cache bit-exact after each compaction."""
+    _need_gpu()
+    from draft_tree_verification_parent_amd.verify_round import VerifyRound
+
+    from _gpu_round import prepared
+    wl, _, w, _, _ = prepared(cfg)  # the session's weights
+    R = 3
+    ri = W.make_round_inputs(wl, extra_slots=R * wl.n_nodes)
+    vr = VerifyRound(ri, w, fused=False, chain=True)
+    rng = np.random.default_rng(500 + cfg)
+    state, moved = ri, 0
+    for rnd in range(R):
+        ts = OR.tree_stage(state)
+        tree = ts["tree"]
+        hidden, _ = W.plant_hidden(wl, lambda ids: w[ids], tree["parent"], tree["token"], tree["n"],
+                                   state.row_off)
+        vr.set_hidden(hidden)
+        vr.run()
+        torch.cuda.synchronize()
+        assert vr.err.item() == 0, f"round {rnd}"
+        assert np.array_equal(vr.table.cpu().numpy(), ts["table"]), f"round {rnd}: table"
+        if vr.tmpl_rows:
+            assert np.array_equal(vr.ret_token[: vr.tmpl_rows].cpu().numpy(), ts["ret_token"])
+        g = vr.tree_host()
+        for key in ("n", "parent", "token", "depth", "pos", "mask", "src"):
+            assert np.array_equal(g[key], tree[key]), f"round {rnd}: {key}"
+        # attention reads this round's context and (compacted) cache
+        nodes = _sample_nodes(rng, tree["n"], 6)
+        q = OL.bf16_to_f64(state.q).reshape(state.q.shape)
+        out = bf16_tensor_to_f64(vr.attn_out)
+        for b in sorted({b for b, _ in nodes}):
+            KL, VL = [None] * state.B, [None] * state.B
+            KL[b], VL[b] = OR.kv_f64(state, b)
+            ref = OA.tree_attention(q, KL, VL, state.ctx_len, tree["n"], state.row_off, tree["mask"],
+                                    state.scale, nodes=[(bb, i) for bb, i in nodes if bb == b])
+            for (bb, i), (o, _) in ref.items():
+                ok, e = within_tol(out[int(state.row_off[bb]) + i], o)
+                assert ok, f"round {rnd}: attention row {(bb, i)} max err {e}"
+        # ranking decisions on the GPU's own fp32 logits
+        ids, _ = OT.topk(vr.logits.cpu().numpy(), state.k)
+        assert np.array_equal(vr.topk_id.cpu().numpy(), ids), f"round {rnd}: top-k"
+        lens, paths, bonus = OAcc.accept_batch(tree["n"], state.row_off, tree["parent"], tree["token"], ids[:, 0])
+        assert vr.acc_len.cpu().numpy().tolist() == lens
+        assert vr.bonus.cpu().numpy().tolist() == bonus
+        # compaction and the next round's inputs
+        nxt = OR.next_round_inputs(state, ts, ids, lens, paths, bonus)
+        shape = state.kcache.shape
+        gk = vr.kcache.view(torch.int16).cpu().numpy().view(np.uint16).reshape(shape)
+        gv = vr.vcache.view(torch.int16).cpu().numpy().view(np.uint16).reshape(shape)
+        assert np.array_equal(gk, nxt.kcache), f"round {rnd}: K cache after compaction"
+        assert np.array_equal(gv, nxt.vcache), f"round {rnd}: V cache after compaction"
+        assert vr.ctx_len.cpu().numpy().tolist() == nxt.ctx_len.tolist()
+        assert vr.root_token.cpu().numpy().tolist() == nxt.root_token.tolist()
+        assert np.array_equal(vr.cand_token.cpu().numpy(), nxt.cand_token)
+        moved += sum(lens)
+        state = nxt
+    assert moved > 0  # the planted target accepts drafts, so rows did move
+    say(f"[chain] cfg {cfg}: {R} chained rounds match the oracle; contexts {state.ctx_len.tolist()[:4]}")
+
+
+def test_chained_graph_replay_matches_eager():
+    """Chained rounds captured two per HIP graph (the context / root buffer
+    pairs swap inside the graph) replay exactly as the same rounds issued
+    eagerly, compacted K/V cache included."""
+    _need_gpu()
+    from draft_tree_verification_parent_amd.verify_round import VerifyRound
+
+    from _gpu_round import prepared
+    wl, _, w, _, hidden = prepared(2)
+    ri = W.make_round_inputs(wl, extra_slots=12 * wl.n_nodes)
+    eager = VerifyRound(ri, w, fused=True, chain=True)
+    graph = VerifyRound(ri, w, fused=True, chain=True)
+    for vr in (eager, graph):
+        vr.set_hidden(hidden)
+        vr.run()
+    with pytest.raises(ValueError):
+        graph.capture(3)
+    graph.capture(2)
+    for rep in range(3):
+        eager.run()
+        eager.run()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name in ("table", "n_out", "parent", "token", "topk_id", "acc_len", "acc_path", "bonus", "ctx_len",
+                     "root_token", "cand_token", "kcache", "vcache", "err"):
+            a, b = getattr(eager, name), getattr(graph, name)
+            assert torch.equal(a, b), f"replay {rep + 1}: {name}"
+    say(f"[chain-graph] contexts after 7 rounds: {graph.ctx_len.cpu().numpy().tolist()}")
