@@ -31,6 +31,8 @@ Modules:
   lmhead     -- logits = hidden . W^T
   topk       -- per-row top-k / argmax, ties to the lower id
   accept     -- greedy acceptance: deepest accepted node, path, bonus token
+  sample     -- acceptance at temperature T > 0: Gumbel-max draws per node,
+                first matching child (a reading: the pages give no rule)
   kv         -- KV compaction to the accepted path and round chaining
   round      -- the above composed into one round
 """

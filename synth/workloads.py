@@ -345,6 +345,14 @@ def make_qkv(ri: RoundInputs, extra_slots: int = 0) -> None:
     ri.vcache = vc
 
 
+def gumbel_noise(cfg: int, name: str, shape) -> np.ndarray:
+    """Seeded i.i.d. Gumbel(0, 1) noise, fp32: -log(-log(u)) of uniforms
+    drawn in fp64 (the random input of sampling at temperature T > 0)."""
+    u = rng(cfg, f"gumbel/{name}").random(shape)
+    u = np.clip(u, 1e-300, 1.0 - 1e-16)
+    return (-np.log(-np.log(u))).astype(np.float32)
+
+
 # ----------------------------------------------------------------------------
 # lm-head weights and planted hidden states
 # ----------------------------------------------------------------------------
