@@ -29,6 +29,10 @@ SIGNATURES = {
     "graft_lmhead_pack_bytes": (c_size_t, [c_int, c_int]),
     "graft_lmhead_pack": (c_int, [c_int, c_int, P, P, P]),
     "graft_accept": (c_int, [c_int, P, P, P, P, P, c_int, P, P, P, P, P]),
+    "graft_lmhead_sample_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),
+    "graft_lmhead_topk_sample": (c_int, [c_int, c_int, c_int, c_int, c_float, P, P, P, P, P, P, P, c_size_t, P]),
+    "graft_sample_rows": (c_int, [c_int, c_int, c_float, P, P, P, P]),
+    "graft_accept_sampled": (c_int, [c_int, P, P, P, P, P, P, P, P, P, P]),
     "graft_kv_compact": (c_int, [c_int, c_int, c_int, c_int, P, P, c_int64, P, c_int64, P, P, P, P, P, P, P, P,
                                  P]),
     "graft_make_template": (c_int, [c_int, c_int, c_int, P, P]),

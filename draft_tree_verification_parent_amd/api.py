@@ -121,6 +121,35 @@ def graft_accept(n, row_off, parent, token, topk_id, k, acc_len, acc_path, bonus
                 _p(bonus, "i32", "bonus"), _p(err, "i32", "err"), _s(stream))
 
 
+def graft_lmhead_sample_workspace_bytes(M, V, k):
+    return int(N.lib().graft_lmhead_sample_workspace_bytes(int(M), int(V), int(k)))
+
+
+def graft_lmhead_topk_sample(M, H, V, k, temperature, hidden, w_packed, gumbel, topk_id, topk_val, sample_id, ws,
+                             stream=None):
+    """Fused packed lm-head: per-row top-k and one Gumbel-max draw at
+    `temperature` (noise `gumbel` fp32 [M, V])."""
+    return call("graft_lmhead_topk_sample", int(M), int(H), int(V), int(k), float(temperature),
+                _p(hidden, "bf16", "hidden"), _p(w_packed, "bf16", "w_packed"), _p(gumbel, "f32", "gumbel"),
+                _p(topk_id, "i32", "topk_id"), _p(topk_val, "f32", "topk_val"), _p(sample_id, "i32", "sample_id"),
+                None if ws is None else ws.data_ptr(), 0 if ws is None else ws.numel() * ws.element_size(),
+                _s(stream))
+
+
+def graft_sample_rows(temperature, logits, gumbel, sample_id, stream=None):
+    M, V = logits.shape
+    return call("graft_sample_rows", int(M), int(V), float(temperature), _p(logits, "f32", "logits"),
+                _p(gumbel, "f32", "gumbel"), _p(sample_id, "i32", "sample_id"), _s(stream))
+
+
+def graft_accept_sampled(n, row_off, parent, token, sample_id, acc_len, acc_path, bonus, err=None, stream=None):
+    B = n.numel()
+    return call("graft_accept_sampled", B, _p(n, "i32", "n"), _p(row_off, "i32", "row_off"),
+                _p(parent, "i32", "parent"), _p(token, "i32", "token"), _p(sample_id, "i32", "sample_id"),
+                _p(acc_len, "i32", "acc_len"), _p(acc_path, "i32", "acc_path"), _p(bonus, "i32", "bonus"),
+                _p(err, "i32", "err"), _s(stream))
+
+
 def graft_kv_compact(Hkv, d, kcache, vcache, kv_off, kv_head_stride, ctx_len, n, acc_len, acc_path, bonus,
                      ctx_next, root_next, n_layers=1, layer_stride=0, err=None, stream=None):
     """Moves each request's accepted path K/V to slots ctx..ctx+a (every

@@ -12,10 +12,18 @@
 // the path length: both come from six rounds of pointer jumping, the
 // deepest accepted node from a wave max-reduction of (depth, -index), and
 // the path from that node's ancestor bitmask.
+//
+// Sampling at temperature T > 0 (FIRST_MATCH): "argmax" is the token drawn at
+// each node, and only the lowest-index child matching its parent's draw is
+// accepted, so the accepted set is one chain and every emitted token follows
+// the target's distribution (rejection sampling keeps it unchanged: TreeGraft
+// page, section 3 and its reading list; the rule for several children is
+// this library's reading, the pages give none).
 #include "common.h"
 
 namespace {
 
+template <bool FIRST_MATCH>
 __global__ __launch_bounds__(64) void accept_kernel(const int32_t *__restrict__ n_arr,
                                                     const int32_t *__restrict__ row_off,
                                                     const int32_t *__restrict__ parent,
@@ -61,6 +69,16 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t *__restrict__ 
   // edge test: my token against my parent's argmax
   const int parent_am = __shfl(am, par >= 0 ? par : lane);
   int ok = (lane == 0) ? 1 : (valid && tok == parent_am ? 1 : 0);
+  if constexpr (FIRST_MATCH) {
+    // an earlier sibling that matches the same draw takes it
+    const int mk = (ok && lane > 0) ? par : -2;
+    int earlier = 0;
+    for (int o = 1; o < n; ++o) {
+      const int v = __builtin_amdgcn_readlane(mk, o);
+      earlier |= (o < lane && v == par) ? 1 : 0;
+    }
+    if (earlier) ok = 0;
+  }
   int dep = (valid && lane > 0) ? 1 : 0;
   uint64_t anc = valid ? (1ull << lane) : 0ull;
   int p = par;
@@ -107,7 +125,21 @@ extern "C" int graft_accept(int B, const int32_t *n, const int32_t *row_off, con
   if (!n || !row_off || !parent || !token || !topk_id || !acc_len || !acc_path || !bonus)
     return fail(GRAFT_EINVAL, "accept: NULL array");
   graft::clear_error();
-  hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(64), 0, graft::as_stream(stream), n, row_off, parent,
+  hipLaunchKernelGGL(accept_kernel<false>, dim3(B), dim3(64), 0, graft::as_stream(stream), n, row_off, parent,
                      token, topk_id, k, acc_len, acc_path, bonus, err_flag);
   return graft::check_launch("accept");
+}
+
+extern "C" int graft_accept_sampled(int B, const int32_t *n, const int32_t *row_off, const int32_t *parent,
+                                    const int32_t *token, const int32_t *sample_id, int32_t *acc_len,
+                                    int32_t *acc_path, int32_t *bonus, int32_t *err_flag, graft_stream stream) {
+  using graft::fail;
+  if (B < 0) return fail(GRAFT_EINVAL, "accept_sampled: B=%d", B);
+  if (B == 0) return GRAFT_OK;
+  if (!n || !row_off || !parent || !token || !sample_id || !acc_len || !acc_path || !bonus)
+    return fail(GRAFT_EINVAL, "accept_sampled: NULL array");
+  graft::clear_error();
+  hipLaunchKernelGGL(accept_kernel<true>, dim3(B), dim3(64), 0, graft::as_stream(stream), n, row_off, parent,
+                     token, sample_id, 1, acc_len, acc_path, bonus, err_flag);
+  return graft::check_launch("accept_sampled");
 }

@@ -298,13 +298,22 @@ __device__ __host__ inline PkMap pk_map(int block, int T) {
 // [w * 128 / PW, (w + 1) * 128 / PW) of each tile and all 64 hidden rows.
 // Larger per-wave tiles need fewer LDS fragment reads per MFMA (2 waves:
 // 8 reads per 16 MFMAs; 4 waves: 6 per 8).
-template <bool FUSED, int K, int PW>
+//
+// SAMPLE (fused only): each row also draws a token at temperature T by the
+// Gumbel-max identity, argmax_t fl(fl(l_t * inv_temp) + g_t) with the noise
+// g read from `gumbel` [M, V]; one running best key per thread, one per
+// (row, workgroup) into part_sample.  The noise loads are ordinary vector
+// loads, so at each tile end their wait also drains the ring's DMAs.
+template <bool FUSED, int K, int PW, bool SAMPLE>
 __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H, int V, int k,
                                                                  const graft_bf16 *__restrict__ hidden,
                                                                  const unsigned char *__restrict__ wpk,
                                                                  float *__restrict__ logits,
                                                                  uint64_t *__restrict__ part_out, int tiles_m,
-                                                                 int tiles_v) {
+                                                                 int tiles_v, float inv_temp,
+                                                                 const float *__restrict__ gumbel,
+                                                                 uint64_t *__restrict__ part_sample) {
+  static_assert(FUSED || !SAMPLE, "sampling rides on the fused epilogue");
   constexpr int NT = PW * 64;
   constexpr int VW = PK_BV / PW;      // vocabulary rows per wave
   constexpr int VBW = VW / 16;        // 16-row MFMA blocks per wave
@@ -363,6 +372,7 @@ __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H,
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   graft::TopKeys<K> L;
   L.init();
+  uint64_t sbest = 0;  // SAMPLE: best perturbed key of this thread's entries
 
   if (Q > 0) issue(0);
   if (Q > 1) issue(1);
@@ -424,6 +434,21 @@ __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H,
         xv[j4 + 1] = vb0 + j4 + 1 < V ? x.y : -INFINITY;
         xv[j4 + 2] = vb0 + j4 + 2 < V ? x.z : -INFINITY;
         xv[j4 + 3] = vb0 + j4 + 3 < V ? x.w : -INFINITY;
+      }
+      if constexpr (SAMPLE) {
+        const int ms = m0 + row;
+        if (ms < M) {
+          const float *gr = gumbel + static_cast<size_t>(ms) * V + vb0;
+#pragma unroll
+          for (int j = 0; j < VPT; ++j) {
+            if (vb0 + j < V) {
+              float sc = __fadd_rn(__fmul_rn(xv[j], inv_temp), gr[j]);
+              sc = sc != sc ? -INFINITY : sc;  // NaN ranks below every number
+              const uint64_t key = graft::rank_key(sc, vb0 + j);
+              sbest = key > sbest ? key : sbest;
+            }
+          }
+        }
       }
       float gm[GPT];
 #pragma unroll
@@ -495,6 +520,10 @@ __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H,
       const uint64_t best = graft::group_max<TPR>(L.k[0]);
       if (L.k[0] == best) L.pop_front();
       if (part == 0 && m < M) part_out[(static_cast<size_t>(m) * S + map.stream) * k + j] = best;
+    }
+    if constexpr (SAMPLE) {
+      const uint64_t best = graft::group_max<TPR>(sbest);
+      if (part == 0 && m < M) part_sample[static_cast<size_t>(m) * S + map.stream] = best;
     }
   }
 }
@@ -587,8 +616,8 @@ extern "C" int graft_lmhead_topk(int M, int H, int V, int k, const graft_bf16 *h
     auto launch = [&](auto fused_tag, auto k_tag, uint64_t *pk) {
       constexpr bool F = decltype(fused_tag)::value;
       constexpr int Kv = decltype(k_tag)::value;
-      hipLaunchKernelGGL((lmhead_packed_kernel<F, Kv, PK_WAVES>), dim3(PK_GRID), dim3(PK_WAVES * 64), 0, s, M, H, V, F ? k : 0,
-                         hidden, wpk, F ? nullptr : logits, pk, tiles_m, tiles_v);
+      hipLaunchKernelGGL((lmhead_packed_kernel<F, Kv, PK_WAVES, false>), dim3(PK_GRID), dim3(PK_WAVES * 64), 0, s, M, H, V,
+                         F ? k : 0, hidden, wpk, F ? nullptr : logits, pk, tiles_m, tiles_v, 1.0f, nullptr, nullptr);
     };
     if (fused) {
       uint64_t *pk = static_cast<uint64_t *>(ws);
@@ -635,4 +664,62 @@ extern "C" int graft_lmhead_topk(int M, int H, int V, int k, const graft_bf16 *h
   }
   if (k > 0) return graft::launch_topk(M, V, k, logits, topk_id, topk_val, ws, s);
   return GRAFT_OK;
+}
+
+namespace {
+size_t packed_sample_ws_bytes(int M, int k) {
+  const int T = packed_tiles_m(M);
+  if (T > PK_GRID) return 0;
+  const size_t S = static_cast<size_t>(pk_map(0, T).streams);
+  const size_t topk = static_cast<size_t>(M) * S * k * sizeof(uint64_t);
+  const size_t samp = static_cast<size_t>(M) * S * sizeof(uint64_t);
+  return topk + samp;
+}
+}  // namespace
+
+extern "C" size_t graft_lmhead_sample_workspace_bytes(int M, int V, int k) {
+  if (M <= 0 || V <= 0 || k <= 0 || k > GRAFT_MAX_K) return 0;
+  return packed_sample_ws_bytes(M, k);
+}
+
+extern "C" int graft_lmhead_topk_sample(int M, int H, int V, int k, float temperature, const graft_bf16 *hidden,
+                                        const graft_bf16 *w_packed, const float *gumbel, int32_t *topk_id,
+                                        float *topk_val, int32_t *sample_id, void *ws, size_t ws_bytes,
+                                        graft_stream stream) {
+  using graft::fail;
+  if (M < 0 || V <= 0 || k < 1 || k > GRAFT_MAX_K || k > V)
+    return fail(GRAFT_EINVAL, "lmhead_topk_sample: M=%d V=%d k=%d", M, V, k);
+  if (!(temperature > 0.f) || !(temperature < INFINITY))
+    return fail(GRAFT_EINVAL, "lmhead_topk_sample: temperature must be positive and finite");
+  if (H <= 0 || H % PK_KC != 0)
+    return fail(GRAFT_EINVAL, "lmhead_topk_sample: H=%d must be a positive multiple of %d", H, PK_KC);
+  if (packed_tiles_m(M) > PK_GRID)
+    return fail(GRAFT_EINVAL, "lmhead_topk_sample: M=%d exceeds the packed path's %d rows", M, PK_GRID * BM);
+  if (static_cast<size_t>(M) * H * 2 > 0xFFFFFFFFull)
+    return fail(GRAFT_EINVAL, "lmhead_topk_sample: hidden of %d x %d exceeds 4 GiB (32-bit DMA offsets)", M, H);
+  if (M == 0) return GRAFT_OK;
+  if (!hidden || !w_packed || !gumbel || !topk_id || !sample_id)
+    return fail(GRAFT_EINVAL, "lmhead_topk_sample: NULL array");
+  const size_t need = packed_sample_ws_bytes(M, k);
+  if (ws_bytes < need || !ws) return fail(GRAFT_EINVAL, "lmhead_topk_sample: workspace %zu bytes < %zu", ws_bytes, need);
+  graft::clear_error();
+  hipStream_t s = graft::as_stream(stream);
+  const int tiles_m = packed_tiles_m(M);
+  const int tiles_v = (V + PK_BV - 1) / PK_BV;
+  const int S = pk_map(0, tiles_m).streams;
+  uint64_t *pk = static_cast<uint64_t *>(ws);
+  uint64_t *ps = pk + static_cast<size_t>(M) * S * k;
+  const float inv_temp = 1.0f / temperature;
+  const unsigned char *wpk = reinterpret_cast<const unsigned char *>(w_packed);
+  if (k <= 8)
+    hipLaunchKernelGGL((lmhead_packed_kernel<true, 8, PK_WAVES, true>), dim3(PK_GRID), dim3(PK_WAVES * 64), 0, s, M, H, V,
+                       k, hidden, wpk, nullptr, pk, tiles_m, tiles_v, inv_temp, gumbel, ps);
+  else
+    hipLaunchKernelGGL((lmhead_packed_kernel<true, 16, PK_WAVES, true>), dim3(PK_GRID), dim3(PK_WAVES * 64), 0, s, M, H,
+                       V, k, hidden, wpk, nullptr, pk, tiles_m, tiles_v, inv_temp, gumbel, ps);
+  int rc = graft::check_launch("lmhead (packed, fused top-k + sample)");
+  if (rc != GRAFT_OK) return rc;
+  rc = graft::launch_topk_merge(M, S, k, pk, topk_id, topk_val, s);
+  if (rc != GRAFT_OK) return rc;
+  return graft::launch_topk_merge(M, S, 1, ps, sample_id, nullptr, s);
 }

@@ -118,6 +118,48 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(int S, int k, cons
   }
 }
 
+// One draw per row at temperature T by the Gumbel-max identity on
+// materialised logits: argmax_t fl(fl(l_t * inv_temp) + g_t), ties to the
+// lower id, NaN below every number.  One 256-thread workgroup per row.
+__global__ __launch_bounds__(kThreads) void sample_rows_kernel(int V, float inv_temp, const float *__restrict__ logits,
+                                                               const float *__restrict__ gumbel,
+                                                               int32_t *__restrict__ sample_id) {
+  __shared__ uint64_t s_best[kThreads / 64];
+  const int m = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float *lr = logits + static_cast<size_t>(m) * V;
+  const float *gr = gumbel + static_cast<size_t>(m) * V;
+  uint64_t best = 0;
+  for (int t0 = 0; t0 < V; t0 += kThreads * 4) {
+    float l[4], g[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u * kThreads + tid;
+      l[u] = t < V ? lr[t] : 0.f;
+      g[u] = t < V ? gr[t] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u * kThreads + tid;
+      if (t < V) {
+        float sc = __fadd_rn(__fmul_rn(l[u], inv_temp), g[u]);
+        sc = sc != sc ? -INFINITY : sc;
+        const uint64_t key = graft::rank_key(sc, t);
+        best = key > best ? key : best;
+      }
+    }
+  }
+  best = graft::group_max<64>(best);
+  if ((tid & 63) == 0) s_best[tid >> 6] = best;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t b = s_best[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) b = s_best[w] > b ? s_best[w] : b;
+    sample_id[m] = graft::key_id(b);
+  }
+}
+
 }  // namespace
 
 namespace graft {
@@ -162,3 +204,17 @@ int launch_topk_merge(int M, int slices, int k, const uint64_t *part, int32_t *t
 }
 
 }  // namespace graft
+
+extern "C" int graft_sample_rows(int M, int V, float temperature, const float *logits, const float *gumbel,
+                                 int32_t *sample_id, graft_stream stream) {
+  using graft::fail;
+  if (M < 0 || V <= 0 || M > 0x7FFFFFFF) return fail(GRAFT_EINVAL, "sample_rows: M=%d V=%d", M, V);
+  if (!(temperature > 0.f) || !(temperature < INFINITY))
+    return fail(GRAFT_EINVAL, "sample_rows: temperature must be positive and finite");
+  if (M == 0) return GRAFT_OK;
+  if (!logits || !gumbel || !sample_id) return fail(GRAFT_EINVAL, "sample_rows: NULL array");
+  graft::clear_error();
+  hipLaunchKernelGGL(sample_rows_kernel, dim3(M), dim3(kThreads), 0, graft::as_stream(stream), V, 1.0f / temperature,
+                     logits, gumbel, sample_id);
+  return graft::check_launch("sample_rows");
+}

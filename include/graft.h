@@ -13,6 +13,9 @@
  *   graft_lmhead_topk            logits = hidden . W^T and per-row top-k
  *                                (weights packed once by graft_lmhead_pack)
  *   graft_accept                 deepest greedily accepted path + bonus token
+ *   graft_lmhead_topk_sample,    (temperature T > 0) one draw per row by
+ *   graft_accept_sampled         Gumbel-max with the noise as an input, and
+ *                                acceptance of the first matching child
  *   graft_kv_compact             (round chaining) the accepted path's K/V
  *                                moves to the front of the tree slots, the
  *                                context advances, the bonus becomes the
@@ -259,6 +262,50 @@ int graft_accept(int B, const int32_t *n, const int32_t *row_off,
                  const int32_t *parent, const int32_t *token, const int32_t *topk_id, int k,
                  int32_t *acc_len, int32_t *acc_path, int32_t *bonus, int32_t *err_flag,
                  graft_stream stream);
+
+/*
+ * Sampling at temperature T > 0.  Verification by rejection sampling keeps
+ * the target's output distribution (TreeGraft page, section 3 and its
+ * reading list); the pages evaluate at T = 1 as well as T = 0 (Graft page,
+ * section 5) but give no rule for a node with several children.  This
+ * library's reading, lossless for a draft tree whose tokens are chosen:
+ * every node draws y ~ softmax(logits / T); the path moves to the
+ * lowest-index child whose token is the parent's draw and stops at the first
+ * node where none is; that draw is the bonus token.
+ *
+ * Draws use the Gumbel-max identity with the noise as an input:
+ *   y[r] = argmax_t s(r, t),  s(r, t) = fl(fl(l(r, t) * fl(1/T)) + g[r * V + t])
+ * (two fp32 operations, each rounded to nearest; ties to the lower t; a
+ * NaN score ranks below every number).  g (device fp32 [M, V]) holds
+ * i.i.d. Gumbel(0, 1) noise, fresh for every round.  temperature: positive
+ * and finite (T = 0 is graft_lmhead_topk + graft_accept).
+ *
+ * graft_lmhead_topk_sample: the fused, packed lm-head of graft_lmhead_topk
+ * (w_packed from graft_lmhead_pack, H % 128 == 0, M <= 16384) producing in
+ * the same pass over W the top-k (topk_id, topk_val as graft_lmhead_topk:
+ * the successor table still takes the target's top-k) and sample_id
+ * (device int32 [M]).  ws: graft_lmhead_sample_workspace_bytes(M, V, k).
+ * The logits are identical to graft_lmhead_topk's, so the draws equal
+ * graft_sample_rows on the logits graft_lmhead_topk materialises.
+ *
+ * graft_sample_rows: the same draws on materialised logits (device fp32
+ * [M, V]).
+ *
+ * graft_accept_sampled: graft_accept with sample_id (device int32, one per
+ * row of the padded layout) in place of the argmax and only the lowest-index
+ * matching child accepted; outputs and error handling as graft_accept,
+ * bonus[b] = sample_id at the last accepted node.
+ */
+size_t graft_lmhead_sample_workspace_bytes(int M, int V, int k);
+int graft_lmhead_topk_sample(int M, int H, int V, int k, float temperature, const graft_bf16 *hidden,
+                             const graft_bf16 *w_packed, const float *gumbel, int32_t *topk_id,
+                             float *topk_val, int32_t *sample_id, void *ws, size_t ws_bytes,
+                             graft_stream stream);
+int graft_sample_rows(int M, int V, float temperature, const float *logits, const float *gumbel,
+                      int32_t *sample_id, graft_stream stream);
+int graft_accept_sampled(int B, const int32_t *n, const int32_t *row_off, const int32_t *parent,
+                         const int32_t *token, const int32_t *sample_id, int32_t *acc_len,
+                         int32_t *acc_path, int32_t *bonus, int32_t *err_flag, graft_stream stream);
 
 /*
  * KV compaction and round chaining (Graft page, section 2, third step: the

@@ -146,3 +146,31 @@ def test_kv_compact_host_validation_launches_nothing(native):
     a = list(args())
     a[14] = None                                                 # ctx_next NULL
     assert L.graft_kv_compact(*a) == E
+
+
+def test_sampling_host_validation_launches_nothing(native):
+    L = native.lib()
+    E = native.GRAFT_EINVAL
+    p = 1
+    ok_ws = 1 << 30
+    # graft_lmhead_topk_sample(M, H, V, k, T, hidden, w, gumbel, ids, vals, sample, ws, ws_bytes, stream)
+    assert L.graft_lmhead_topk_sample(4, 256, 100, 4, 0.0, p, p, p, p, p, p, p, ok_ws, None) == E   # T = 0
+    assert L.graft_lmhead_topk_sample(4, 256, 100, 4, float("nan"), p, p, p, p, p, p, p, ok_ws, None) == E
+    assert L.graft_lmhead_topk_sample(4, 256, 100, 4, float("inf"), p, p, p, p, p, p, p, ok_ws, None) == E
+    assert L.graft_lmhead_topk_sample(4, 200, 100, 4, 1.0, p, p, p, p, p, p, p, ok_ws, None) == E   # H % 128
+    assert L.graft_lmhead_topk_sample(4, 256, 100, 0, 1.0, p, p, p, p, p, p, p, ok_ws, None) == E   # k = 0
+    assert L.graft_lmhead_topk_sample(4, 256, 100, 17, 1.0, p, p, p, p, p, p, p, ok_ws, None) == E
+    assert L.graft_lmhead_topk_sample(4, 256, 100, 4, 1.0, p, p, None, p, p, p, p, ok_ws, None) == E  # no noise
+    assert L.graft_lmhead_topk_sample(4, 256, 100, 4, 1.0, p, p, p, p, p, p, p, 8, None) == E  # workspace
+    assert L.graft_lmhead_topk_sample(0, 256, 100, 4, 1.0, None, None, None, None, None, None, None, 0, None) == 0
+    assert L.graft_lmhead_sample_workspace_bytes(60, 1000, 8) > L.graft_lmhead_topk_workspace_bytes(60, 1000, 8) - 1
+    assert L.graft_lmhead_sample_workspace_bytes(60, 1000, 0) == 0
+    # graft_sample_rows(M, V, T, logits, gumbel, sample, stream)
+    assert L.graft_sample_rows(4, 100, -1.0, p, p, p, None) == E
+    assert L.graft_sample_rows(4, 0, 1.0, p, p, p, None) == E
+    assert L.graft_sample_rows(4, 100, 1.0, p, None, p, None) == E
+    assert L.graft_sample_rows(0, 100, 1.0, None, None, None, None) == 0
+    # graft_accept_sampled(B, n, row_off, parent, token, sample, len, path, bonus, err, stream)
+    assert L.graft_accept_sampled(-1, p, p, p, p, p, p, p, p, None, None) == E
+    assert L.graft_accept_sampled(2, p, p, p, p, None, p, p, p, None, None) == E
+    assert L.graft_accept_sampled(0, None, None, None, None, None, None, None, None, None, None) == 0

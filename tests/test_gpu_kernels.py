@@ -6,6 +6,7 @@ import pytest
 from oracle import OracleError
 from oracle import accept as OAcc
 from oracle import kv as OKV
+from oracle import sample as OS
 from oracle import attention as OA
 from oracle import lmhead as OL
 from oracle import table as OTab
@@ -207,6 +208,109 @@ def test_fused_packed_topk_equals_split(api, M, H, V, k):
     eid, ev = OT.topk(logits.cpu().numpy(), k)
     assert np.array_equal(ids.cpu().numpy(), eid)
     assert np.array_equal(vals.cpu().numpy(), ev)
+
+
+# ----------------------------------------------------------------------------- sampling (T > 0)
+
+@pytest.mark.parametrize("T", [0.6, 1.0, 1.7])
+def test_sample_rows_matches_oracle(api, T):
+    """Gumbel-max draws on given fp32 logits: the same fp32 operations on
+    both sides, so the ids agree exactly; NaN rows, constant rows (ties to
+    the lowest id) and -inf entries included."""
+    r = np.random.default_rng(int(T * 100))
+    M, V = 37, 50_000
+    logits = (2.0 * r.standard_normal((M, V))).astype(np.float32)
+    logits[3] = np.float32(0.25)                # constant row
+    logits[5, ::7] = np.nan                     # NaN entries never win
+    logits[6, :] = -np.inf                      # all -inf: id 0
+    g = W.gumbel_noise(1, f"rows{T}", (M, V))
+    g[3] = 0.0                                  # constant row, no noise: ties -> id 0
+    out = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    api.graft_sample_rows(T, torch.from_numpy(logits).cuda(), torch.from_numpy(g).cuda(), out)
+    torch.cuda.synchronize()
+    exp = OS.sample_rows(logits, T, g)
+    assert np.array_equal(out.cpu().numpy(), exp)
+    assert exp[3] == 0 and exp[6] == 0
+
+
+@pytest.mark.parametrize("M,H,V,k,T", [(60, 4096, 128256, 8, 1.0), (130, 384, 1001, 16, 0.7), (1, 128, 5, 3, 2.0),
+                                       (2112, 128, 300, 8, 1.0)])
+def test_fused_sampling_equals_split(api, M, H, V, k, T):
+    """The fused lm-head draws exactly what graft_sample_rows (and the
+    oracle, in the same fp32 operations) draws on the logits the split mode
+    writes, and its top-k equals the top-k of those logits."""
+    say(f"[fused lmhead+topk+sample] M={M} H={H} V={V} k={k} T={T}")
+    r = np.random.default_rng(M * 13 + V)
+    h = f32_to_bf16_bits(r.standard_normal((M, H)).astype(np.float32))
+    w = f32_to_bf16_bits((0.02 * r.standard_normal((V, H))).astype(np.float32))
+    hd = dev_bf16(h)
+    wd, wp = _packed(api, w, V, H)
+    g = W.gumbel_noise(2, f"fused{M}x{V}", (M, V))
+    gd = torch.from_numpy(g).cuda()
+    logits = torch.empty(M, V, dtype=torch.float32, device="cuda")
+    api.graft_lmhead_topk(M, H, V, 0, hd, wd, logits)
+    ws = torch.empty(api.graft_lmhead_sample_workspace_bytes(M, V, k), dtype=torch.uint8, device="cuda")
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    vals = torch.empty(M, k, dtype=torch.float32, device="cuda")
+    samp = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    api.graft_lmhead_topk_sample(M, H, V, k, T, hd, wp, gd, ids, vals, samp, ws)
+    split = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    api.graft_sample_rows(T, logits, gd, split)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    exp = OS.sample_rows(lg, T, g)
+    assert np.array_equal(split.cpu().numpy(), exp)
+    assert np.array_equal(samp.cpu().numpy(), exp)
+    eid, ev = OT.topk(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), eid)
+    assert np.array_equal(vals.cpu().numpy(), ev)
+
+
+def _tree_with_duplicate_siblings(r, n, V):
+    parent = [-1] + [int(r.integers(0, i)) for i in range(1, n)]
+    token = [int(r.integers(0, V))]
+    for i in range(1, n):
+        sib = [token[j] for j in range(1, i) if parent[j] == parent[i]]
+        token.append(sib[0] if sib and r.random() < 0.3 else int(r.integers(0, V)))
+    return parent, token
+
+
+def test_accept_sampled_matches_oracle(api):
+    """First-match acceptance on ragged trees with duplicate siblings; the
+    draws hit a child at most nodes so paths run deep."""
+    r = np.random.default_rng(808)
+    V = 6
+    n, row_off, parent, token, samp = [], [0], [], [], []
+    for b in range(40):
+        nb = int(r.integers(1, 65))
+        p, t = _tree_with_duplicate_siblings(r, nb, V)
+        s = []
+        for u in range(nb):
+            kids = [t[c] for c in range(nb) if p[c] == u]
+            s.append(kids[int(r.integers(0, len(kids)))] if kids and r.random() < 0.8 else int(r.integers(0, V)))
+        cap = nb + int(r.integers(0, 3))
+        pad = cap - nb
+        parent += p + [-1] * pad
+        token += t + [-1] * pad
+        samp += s + [0] * pad
+        n.append(nb)
+        row_off.append(row_off[-1] + cap)
+    B = len(n)
+    out_len = torch.empty(B, dtype=torch.int32, device="cuda")
+    out_path = torch.empty(B, 64, dtype=torch.int32, device="cuda")
+    out_bonus = torch.empty(B, dtype=torch.int32, device="cuda")
+    err = err_buf()
+    api.graft_accept_sampled(dev_i32(n), dev_i32(row_off), dev_i32(parent), dev_i32(token), dev_i32(samp),
+                             out_len, out_path, out_bonus, err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    lens, paths, bonus = OS.accept_sampled_batch(n, row_off, np.array(parent), np.array(token), np.array(samp))
+    assert out_len.cpu().numpy().tolist() == lens
+    assert out_bonus.cpu().numpy().tolist() == bonus
+    gp = out_path.cpu().numpy()
+    for b in range(B):
+        assert gp[b].tolist() == paths[b] + [-1] * (64 - len(paths[b])), b
+    assert max(lens) >= 4
 
 
 # ----------------------------------------------------------------------------- accept
