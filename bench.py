@@ -250,24 +250,48 @@ def main():
     def compact():
         api.graft_kv_compact(wl.Hkv, wl.d, vr.kcache, vr.vcache, vr.kv_off, ri.kv_head_stride, vr.ctx_len,
                              vr.n_out, vr.acc_len, vr.acc_path, vr.bonus, ctx_s, root_s, err=vr.err)
-    for _ in range(3):
-        compact()
-    torch.cuda.synchronize()
-    kv_graph = torch.cuda.CUDAGraph()  # `steps` calls in one graph: kernel time, not host launch time
-    with torch.cuda.graph(kv_graph):
-        for _ in range(args.steps):
-            compact()
-    kv_graph.replay()
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    kv_graph.replay()
-    c1.record()
-    torch.cuda.synchronize()
-    kv_us = c0.elapsed_time(c1) * 1e3 / args.steps
+    def graph_us(fn, calls):
+        """Device time per call of `calls` back-to-back calls captured in one
+        HIP graph (kernel time, not host launch time)."""
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(calls):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / calls
+
+    kv_us = graph_us(compact, args.steps)
     kernels["kv_compact"] = {"us": round(kv_us, 2), "rows_moved": moved, "bytes": kv_bytes,
                              "hbm_frac": round(kv_bytes / (kv_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 6),
                              "note": "round chaining step, timed on its own (not in the round)"}
+
+    # Sampling at T = 1 (graft_lmhead_topk_sample: top-k plus one Gumbel-max
+    # draw per row in the same pass over W; the noise is an input, 4 B per
+    # logit), timed on its own in a graph of calls beside the greedy pass.
+    if vr.w_packed is not None:
+        noise = torch.from_numpy(W.gumbel_noise(args.cfg, "bench", (M, V))).to(vr.dev)
+        sws = torch.empty(api.graft_lmhead_sample_workspace_bytes(M, V, ri.k), dtype=torch.uint8, device=vr.dev)
+        s_id = torch.empty(M, ri.k, dtype=torch.int32, device=vr.dev)
+        s_val = torch.empty(M, ri.k, dtype=torch.float32, device=vr.dev)
+        s_draw = torch.empty(M, dtype=torch.int32, device=vr.dev)
+
+        def sample_pass():
+            api.graft_lmhead_topk_sample(M, H, V, ri.k, 1.0, vr.hidden, vr.w_packed, noise, s_id, s_val, s_draw, sws)
+        s_us = graph_us(sample_pass, args.steps)
+        g_us = graph_us(vr.step_lmhead_topk, args.steps)
+        s_bytes = lm_bytes + M * V * 4
+        kernels["lmhead_topk_sample_T1"] = {
+            "us": round(s_us, 2), "greedy_us_same_timing": round(g_us, 2), "bytes": s_bytes,
+            "hbm_frac": round(s_bytes / (s_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "temperature 1: top-k and one draw per row in one pass; timed on its own (not in the round)"}
 
     cpu = None
     if not args.no_cpu_baseline:

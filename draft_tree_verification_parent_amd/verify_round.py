@@ -30,6 +30,9 @@ from ._native import TREE_PRUNE, TREE_STATIC_REPLACE, W_PACKED, W_ROWMAJOR
 
 STEPS_FUSED = ("update_retrieve", "build_tree", "tree_attention", "lmhead_topk", "accept")
 STEPS_SPLIT = ("update_retrieve", "build_tree", "tree_attention", "lmhead", "topk", "accept")
+# temperature T > 0: one Gumbel-max draw per row, first-match acceptance
+STEPS_FUSED_T = ("update_retrieve", "build_tree", "tree_attention", "lmhead_topk_sample", "accept_sampled")
+STEPS_SPLIT_T = ("update_retrieve", "build_tree", "tree_attention", "lmhead", "topk", "sample", "accept_sampled")
 
 
 def _i32(x, dev):
@@ -43,17 +46,24 @@ def _bf16(bits, dev):
 
 class VerifyRound:
     def __init__(self, ri, w_bits=None, device="cuda", dmax: int = 8, fused: bool = True,
-                 packed: bool = True, chain: bool = False):
+                 packed: bool = True, chain: bool = False, temperature: float = 0.0):
         """fused: lm-head and top-k in one pass (logits never stored);
         packed: the lm-head weight is packed once here (when H % 128 == 0)
         and the fused pass reads the packed copy;
         chain: every round ends with KV compaction and the next round
         starts from its context and root (the cache needs headroom: see
-        synth make_round_inputs(extra_slots=...))."""
+        synth make_round_inputs(extra_slots=...));
+        temperature > 0: acceptance by one draw per node (set_gumbel gives
+        each round's noise) instead of the argmax."""
         dev = torch.device(device)
         self.fused = fused
         self.chain = chain
-        self.steps = (STEPS_FUSED if fused else STEPS_SPLIT) + (("kv_compact",) if chain else ())
+        self.temperature = float(temperature)
+        if self.temperature > 0:
+            base = STEPS_FUSED_T if fused else STEPS_SPLIT_T
+        else:
+            base = STEPS_FUSED if fused else STEPS_SPLIT
+        self.steps = base + (("kv_compact",) if chain else ())
         wl = ri.wl
         self.ri, self.wl, self.dev = ri, wl, dev
         B, N, k, V = ri.B, ri.N, ri.k, ri.V
@@ -126,6 +136,14 @@ class VerifyRound:
         tkb = api.graft_lmhead_topk_workspace_bytes(rows, V, k)
         self.topk_ws = torch.empty(max(tkb, 1), dtype=torch.uint8, device=dev)
 
+        self.sample_id = z(rows)
+        self.gumbel = None
+        self.sample_ws = None
+        if self.temperature > 0 and fused:
+            if self.w_packed is None:
+                raise ValueError("sampling with the fused lm-head needs the packed weight (H % 128 == 0)")
+            self.sample_ws = torch.empty(api.graft_lmhead_sample_workspace_bytes(rows, V, k), dtype=torch.uint8,
+                                         device=dev)
         self.acc_len = z(B)
         self.acc_path = z(B, 64)
         self.bonus = z(B)
@@ -141,6 +159,15 @@ class VerifyRound:
 
     def set_hidden(self, hidden_bits):
         self.hidden = _bf16(hidden_bits.reshape(self.rows, self.wl.H), self.dev)
+
+    def set_gumbel(self, noise):
+        """This round's Gumbel(0, 1) noise, fp32 [rows, V] (temperature > 0).
+        Copied into one fixed buffer, so captured graphs see new noise."""
+        x = torch.from_numpy(np.ascontiguousarray(noise, np.float32).reshape(self.rows, self.V))
+        if self.gumbel is None:
+            self.gumbel = x.to(self.dev)
+        else:
+            self.gumbel.copy_(x)
 
     def chain_update(self):
         """Make the next round's update read this round's verified nodes."""
@@ -183,6 +210,18 @@ class VerifyRound:
     def step_topk(self):
         api.graft_lmhead_topk(self.rows, self.wl.H, self.V, self.k, None, None, self.logits,
                               self.topk_id, self.topk_val, self.topk_ws)
+
+    def step_lmhead_topk_sample(self):
+        api.graft_lmhead_topk_sample(self.rows, self.wl.H, self.V, self.k, self.temperature, self.hidden,
+                                     self.w_packed, self.gumbel, self.topk_id, self.topk_val, self.sample_id,
+                                     self.sample_ws)
+
+    def step_sample(self):
+        api.graft_sample_rows(self.temperature, self.logits, self.gumbel, self.sample_id)
+
+    def step_accept_sampled(self):
+        api.graft_accept_sampled(self.n_out, self.row_off, self.parent, self.token, self.sample_id,
+                                 self.acc_len, self.acc_path, self.bonus, self.err)
 
     def step_kv_compact(self):
         wl = self.wl

@@ -13,6 +13,7 @@ from oracle import accept as OAcc
 from oracle import attention as OA
 from oracle import lmhead as OL
 from oracle import round as OR
+from oracle import sample as OS
 from oracle import topk as OT
 from synth import workloads as W
 
@@ -192,13 +193,15 @@ def test_graph_replay_matches_eager(cfg, per_graph):
     say(f"[graph] cfg {cfg}: 4 replays of {per_graph} round(s) identical to eager rounds")
 
 
-@pytest.mark.parametrize("cfg", [2, 5])
-def test_chained_rounds_match_oracle(cfg):
+@pytest.mark.parametrize("cfg,T", [(2, 0.0), (5, 0.0), (2, 1.0)])
+def test_chained_rounds_match_oracle(cfg, T):
     """Three rounds chained on the GPU (KV compaction, context advance, bonus
     token as the next root) against the oracle's chain, round by round: the
     table, retrieval and tree bit-exact, attention on sampled nodes within
     tolerance over the compacted cache, top-k and acceptance on the GPU's
-    fp32 logits, and the whole K/V cache bit-exact after each compaction."""
+    fp32 logits (at T > 0: the Gumbel-max draws with the same noise and
+    first-match acceptance), and the whole K/V cache bit-exact after each
+    compaction."""
     _need_gpu()
     from draft_tree_verification_parent_amd.verify_round import VerifyRound
 
@@ -206,7 +209,7 @@ def test_chained_rounds_match_oracle(cfg):
     wl, _, w, _, _ = prepared(cfg)  # the session's weights
     R = 3
     ri = W.make_round_inputs(wl, extra_slots=R * wl.n_nodes)
-    vr = VerifyRound(ri, w, fused=False, chain=True)
+    vr = VerifyRound(ri, w, fused=False, chain=True, temperature=T)
     rng = np.random.default_rng(500 + cfg)
     state, moved = ri, 0
     for rnd in range(R):
@@ -215,6 +218,9 @@ def test_chained_rounds_match_oracle(cfg):
         hidden, _ = W.plant_hidden(wl, lambda ids: w[ids], tree["parent"], tree["token"], tree["n"],
                                    state.row_off)
         vr.set_hidden(hidden)
+        noise = W.gumbel_noise(cfg, f"chain{rnd}", (state.B * state.N, state.V)) if T > 0 else None
+        if T > 0:
+            vr.set_gumbel(noise)
         vr.run()
         torch.cuda.synchronize()
         assert vr.err.item() == 0, f"round {rnd}"
@@ -237,9 +243,17 @@ def test_chained_rounds_match_oracle(cfg):
                 ok, e = within_tol(out[int(state.row_off[bb]) + i], o)
                 assert ok, f"round {rnd}: attention row {(bb, i)} max err {e}"
         # ranking decisions on the GPU's own fp32 logits
-        ids, _ = OT.topk(vr.logits.cpu().numpy(), state.k)
+        lg = vr.logits.cpu().numpy()
+        ids, _ = OT.topk(lg, state.k)
         assert np.array_equal(vr.topk_id.cpu().numpy(), ids), f"round {rnd}: top-k"
-        lens, paths, bonus = OAcc.accept_batch(tree["n"], state.row_off, tree["parent"], tree["token"], ids[:, 0])
+        if T > 0:
+            drawn = OS.sample_rows(lg, T, noise)
+            assert np.array_equal(vr.sample_id.cpu().numpy(), drawn), f"round {rnd}: draws"
+            lens, paths, bonus = OS.accept_sampled_batch(tree["n"], state.row_off, tree["parent"], tree["token"],
+                                                         drawn)
+        else:
+            lens, paths, bonus = OAcc.accept_batch(tree["n"], state.row_off, tree["parent"], tree["token"],
+                                                   ids[:, 0])
         assert vr.acc_len.cpu().numpy().tolist() == lens
         assert vr.bonus.cpu().numpy().tolist() == bonus
         # compaction and the next round's inputs
@@ -254,7 +268,8 @@ def test_chained_rounds_match_oracle(cfg):
         assert np.array_equal(vr.cand_token.cpu().numpy(), nxt.cand_token)
         moved += sum(lens)
         state = nxt
-    assert moved > 0  # the planted target accepts drafts, so rows did move
+    if T == 0:
+        assert moved > 0  # the planted target accepts drafts, so rows did move
     say(f"[chain] cfg {cfg}: {R} chained rounds match the oracle; contexts {state.ctx_len.tolist()[:4]}")
 
 
@@ -286,3 +301,29 @@ def test_chained_graph_replay_matches_eager():
             a, b = getattr(eager, name), getattr(graph, name)
             assert torch.equal(a, b), f"replay {rep + 1}: {name}"
     say(f"[chain-graph] contexts after 7 rounds: {graph.ctx_len.cpu().numpy().tolist()}")
+
+
+
+def test_sampled_round_fused_equals_split():
+    """At T = 1 the fused round (top-k and draws in one pass over W) gives the
+    same top-k, draws and acceptance as the split round on the same inputs."""
+    _need_gpu()
+    from draft_tree_verification_parent_amd.verify_round import VerifyRound
+
+    from _gpu_round import prepared
+    wl, ri, w, ts, hidden = prepared(2)
+    noise = W.gumbel_noise(2, "fused-vs-split", (ri.B * ri.N, ri.V))
+    outs = []
+    for fused in (True, False):
+        vr = VerifyRound(ri, w, fused=fused, temperature=1.0)
+        vr.set_hidden(hidden)
+        vr.set_gumbel(noise)
+        vr.run()
+        torch.cuda.synchronize()
+        assert vr.err.item() == 0
+        outs.append({k: getattr(vr, k).cpu().numpy() for k in ("topk_id", "topk_val", "sample_id", "acc_len",
+                                                                "acc_path", "bonus")})
+        del vr
+    for k in outs[0]:
+        assert np.array_equal(outs[0][k], outs[1][k]), k
+    say(f"[sampled round] fused = split; accepted lengths {outs[0]['acc_len'].tolist()}")
