@@ -303,7 +303,8 @@ __device__ __host__ inline PkMap pk_map(int block, int T) {
 // Gumbel-max identity, argmax_t fl(fl(l_t * inv_temp) + g_t) with the noise
 // g read from `gumbel` [M, V]; one running best key per thread, one per
 // (row, workgroup) into part_sample.  The noise loads are ordinary vector
-// loads, so at each tile end their wait also drains the ring's DMAs.
+// loads whose wait also covers the ring's older DMAs; they are issued before
+// the tile's top-k work and consumed after it.
 template <bool FUSED, int K, int PW, bool SAMPLE>
 __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H, int V, int k,
                                                                  const graft_bf16 *__restrict__ hidden,
@@ -435,19 +436,26 @@ __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H,
         xv[j4 + 2] = vb0 + j4 + 2 < V ? x.z : -INFINITY;
         xv[j4 + 3] = vb0 + j4 + 3 < V ? x.w : -INFINITY;
       }
+      // SAMPLE: this row's noise is loaded first (16-byte loads while the
+      // thread's 16 columns lie inside the row) and used only after the top-k
+      // work below, so waiting for it (which also waits for the ring's older
+      // DMAs) costs little.  Columns past V re-read column V - 1.
+      float gv[SAMPLE ? VPT : 1];
+      const int ms = m0 + row;
       if constexpr (SAMPLE) {
-        const int ms = m0 + row;
-        if (ms < M) {
-          const float *gr = gumbel + static_cast<size_t>(ms) * V + vb0;
+        const float *grow = gumbel + static_cast<size_t>(ms < M ? ms : M - 1) * V;
+        if (vb0 + VPT <= V && (V & 3) == 0) {
 #pragma unroll
-          for (int j = 0; j < VPT; ++j) {
-            if (vb0 + j < V) {
-              float sc = __fadd_rn(__fmul_rn(xv[j], inv_temp), gr[j]);
-              sc = sc != sc ? -INFINITY : sc;  // NaN ranks below every number
-              const uint64_t key = graft::rank_key(sc, vb0 + j);
-              sbest = key > sbest ? key : sbest;
-            }
+          for (int j4 = 0; j4 < VPT; j4 += 4) {
+            const float4 x = *reinterpret_cast<const float4 *>(grow + vb0 + j4);
+            gv[j4] = x.x;
+            gv[j4 + 1] = x.y;
+            gv[j4 + 2] = x.z;
+            gv[j4 + 3] = x.w;
           }
+        } else {
+#pragma unroll
+          for (int j = 0; j < VPT; ++j) gv[j] = grow[min(vb0 + j, V - 1)];
         }
       }
       float gm[GPT];
@@ -490,6 +498,22 @@ __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H,
           if (pass == 0) break;
           j = jn;
           vj = vn;
+        }
+      }
+      if constexpr (SAMPLE) {
+        // two roundings, as defined: no fused multiply-add
+#pragma clang fp contract(off)
+        if (ms < M) {
+#pragma unroll
+          for (int j = 0; j < VPT; ++j) {
+            if (vb0 + j < V) {
+              const float scaled = xv[j] * inv_temp;
+              float sc = scaled + gv[j];
+              sc = sc != sc ? -INFINITY : sc;  // NaN ranks below every number
+              const uint64_t key = graft::rank_key(sc, vb0 + j);
+              sbest = key > sbest ? key : sbest;
+            }
+          }
         }
       }
     } else {

@@ -140,9 +140,12 @@ __global__ __launch_bounds__(kThreads) void sample_rows_kernel(int V, float inv_
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
+      // two roundings, as defined: no fused multiply-add
+#pragma clang fp contract(off)
       const int t = t0 + u * kThreads + tid;
       if (t < V) {
-        float sc = __fadd_rn(__fmul_rn(l[u], inv_temp), g[u]);
+        const float scaled = l[u] * inv_temp;
+        float sc = scaled + g[u];
         sc = sc != sc ? -INFINITY : sc;
         const uint64_t key = graft::rank_key(sc, t);
         best = key > best ? key : best;

@@ -233,6 +233,40 @@ def test_sample_rows_matches_oracle(api, T):
     assert exp[3] == 0 and exp[6] == 0
 
 
+def _two_roundings_rows(T, rows=24):
+    """Rows of two entries where fl(fl(l * inv) + g) differs from the fused
+    fl(l * inv + g): entry 1 (l = 0) carries exactly one of the two scores
+    of entry 0, so the draw depends on which rounding the kernel does."""
+    from fractions import Fraction
+    r = np.random.default_rng(4242)
+    inv = np.float32(1.0) / np.float32(T)
+    L, G = [], []
+    while len(L) < rows:
+        l0 = np.float32(r.standard_normal() * 3)
+        g0 = np.float32(r.standard_normal() * 3)
+        two = np.float32(np.float32(l0 * inv) + g0)
+        exact = Fraction(float(l0)) * Fraction(float(inv)) + Fraction(float(g0))
+        fused = np.float32(float(exact))  # one rounding (to nearest; ties are measure-zero here)
+        if fused == two or float(exact) != float(Fraction(float(exact))):
+            continue
+        # entry 1 ties entry 0 under the two-rounding definition -> id 0 wins;
+        # under a fused multiply-add entry 0 would score `fused` instead
+        L.append([l0, np.float32(0.0)])
+        G.append([g0, two])
+    return np.array(L, np.float32), np.array(G, np.float32)
+
+
+@pytest.mark.parametrize("T", [0.7, 1.3])
+def test_draws_round_twice_not_fused(api, T):
+    l, g = _two_roundings_rows(T)
+    out = torch.full((len(l),), -1, dtype=torch.int32, device="cuda")
+    api.graft_sample_rows(T, torch.from_numpy(l).cuda(), torch.from_numpy(g).cuda(), out)
+    torch.cuda.synchronize()
+    exp = OS.sample_rows(l, T, g)
+    assert exp.tolist() == [0] * len(l)  # every row a tie under the definition
+    assert out.cpu().numpy().tolist() == exp.tolist()
+
+
 @pytest.mark.parametrize("M,H,V,k,T", [(60, 4096, 128256, 8, 1.0), (130, 384, 1001, 16, 0.7), (1, 128, 5, 3, 2.0),
                                        (2112, 128, 300, 8, 1.0)])
 def test_fused_sampling_equals_split(api, M, H, V, k, T):
