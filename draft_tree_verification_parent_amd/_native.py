@@ -33,6 +33,7 @@ SIGNATURES = {
     "graft_lmhead_topk_sample": (c_int, [c_int, c_int, c_int, c_int, c_float, P, P, P, P, P, P, P, c_size_t, P]),
     "graft_sample_rows": (c_int, [c_int, c_int, c_float, P, P, P, P]),
     "graft_accept_sampled": (c_int, [c_int, P, P, P, P, P, P, P, P, P, P]),
+    "graft_tail_cut": (c_int, [c_int, c_int, P, P, P, c_float, P, P, P]),
     "graft_kv_compact": (c_int, [c_int, c_int, c_int, c_int, P, P, c_int64, P, c_int64, P, P, P, P, P, P, P, P,
                                  P]),
     "graft_make_template": (c_int, [c_int, c_int, c_int, P, P]),
@@ -42,7 +43,7 @@ SIGNATURES = {
 GRAFT_OK, GRAFT_EINVAL, GRAFT_EUNSUPPORTED, GRAFT_EHIP = 0, -1, -2, -3
 ERR_TOKEN, ERR_PARENT, ERR_NOT_CLOSED, ERR_CAPACITY, ERR_RANK = 1, 2, 4, 8, 16
 SRC_ROOT, SRC_DRAFT, SRC_RETRIEVED, SRC_REPLACED = 0, 1, 2, 3
-TREE_PRUNE, TREE_STATIC_REPLACE = 0, 1
+TREE_PRUNE, TREE_STATIC_REPLACE, TREE_TAIL = 0, 1, 2
 W_ROWMAJOR, W_PACKED = 0, 1
 MAX_NODES, MAX_K = 64, 16
 

@@ -150,6 +150,15 @@ def graft_accept_sampled(n, row_off, parent, token, sample_id, acc_len, acc_path
                 _p(err, "i32", "err"), _s(stream))
 
 
+def graft_tail_cut(root_token, block_token, block_conf, tau, keep_len, retrieval_root, stream=None):
+    """Graft-TAIL: per request the kept prefix length of a block draft and
+    the retrieval root (token of the deepest kept node)."""
+    B, L = block_token.shape
+    return call("graft_tail_cut", int(B), int(L), _p(root_token, "i32", "root_token"),
+                _p(block_token, "i32", "block_token"), _p(block_conf, "f32", "block_conf"), float(tau),
+                _p(keep_len, "i32", "keep_len"), _p(retrieval_root, "i32", "retrieval_root"), _s(stream))
+
+
 def graft_kv_compact(Hkv, d, kcache, vcache, kv_off, kv_head_stride, ctx_len, n, acc_len, acc_path, bonus,
                      ctx_next, root_next, n_layers=1, layer_stride=0, err=None, stream=None):
     """Moves each request's accepted path K/V to slots ctx..ctx+a (every

@@ -7,7 +7,11 @@
 // 2, second step).  The hybrid tree is flattened and gets tree positions
 // and a mask (Graft page, section 2, third step).  Static replacement keeps
 // the slot count and swaps low-confidence draft nodes for table successors
-// (Graft page, section 4, batched-serving paragraph).
+// (Graft page, section 4, batched-serving paragraph).  Tail mode (Graft page,
+// section 7, Graft-TAIL on block drafts): the candidates are a block draft
+// with per-token confidences; the prefix up to the first confidence below
+// tau is kept and the freed slots take the first template rows, hung under
+// the deepest kept node.
 //
 // One workgroup of 512 threads per request.  Every input array is staged in
 // LDS by one round of loads.  Ranking works on unique 64-bit keys: each
@@ -141,6 +145,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
   __shared__ int s_wtot[kPasses * kWavesBT];
   __shared__ uint64_t s_m1[4][64], s_m2[2][64], s_m3[64];  // merge partners, one buffer per round
   __shared__ uint64_t s_thr;                                // smallest key kept
+  __shared__ int s_firstlow;                                // tail mode: first block index below tau
   __shared__ int s_np[GRAFT_MAX_NODES];
   __shared__ int s_nt[GRAFT_MAX_NODES];
   __shared__ int s_nsrc[GRAFT_MAX_NODES];
@@ -157,7 +162,8 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
   const int r0 = row_off[b];
   const int rows = row_off[b + 1] - r0;
   const int cap = rows < GRAFT_MAX_NODES ? rows : GRAFT_MAX_NODES;
-  const int R = (mode == GRAFT_TREE_PRUNE && ret_off) ? ret_off[b + 1] - ret_off[b] : 0;
+  const bool tail = mode == GRAFT_TREE_TAIL;
+  const int R = ((mode == GRAFT_TREE_PRUNE || tail) && ret_off) ? ret_off[b + 1] - ret_off[b] : 0;
   const int ro = R > 0 ? ret_off[b] : 0;
   const int bud = budget[b];
   const int ctx = ctx_len[b];
@@ -197,6 +203,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     }
     kreg[pass] = key;
   }
+  if (tid == 0) s_firstlow = C;
   for (int r = tid; r < R && r < GRAFT_MAX_NODES; r += kThreads) {
     s_rpar[r] = ret_parent[ro + r];
     s_rtok[r] = ret_token[ro + r];
@@ -228,8 +235,18 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     const int at = need <= 0 ? 0 : (need < 64 ? need - 1 : 63);
     if (lane64 == at) s_thr = need <= 0 ? ~0ull : top;
   }
+  // tail mode: candidates 0..K are kept, K + 1 = the first block index whose
+  // confidence is below tau (NaN counts as below)
+  if (tail) {
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const int c = pass * kThreads + tid;
+      if (c >= 1 && c < C && !(s_score[c] >= thresh)) atomicMin(&s_firstlow, c);
+    }
+  }
   __syncthreads();
   const uint64_t thr = s_thr;
+  const int firstlow = s_firstlow;
   // exclusive prefix of the keep flags: bit count below this lane within the
   // wavefront, then the totals of the earlier wavefronts
 #pragma unroll
@@ -237,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     if (pass * kThreads < C) {  // uniform
       const int c = pass * kThreads + tid;
       const bool live = c < C;
-      const bool keep = live && (c == 0 || kreg[pass] >= thr);
+      const bool keep = live && (tail ? c < firstlow : (c == 0 || kreg[pass] >= thr));
       const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
       const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
@@ -261,7 +278,10 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
   }
   __syncthreads();
 
-  const int n = nd + R;
+  // tail mode: the retrieved rows fill the budget left after the kept prefix
+  // (the template's first rows are the smaller templates)
+  const int Rk = tail ? max(0, min(R, bud - nd)) : R;
+  const int n = nd + Rk;
   if (n > cap) {
     if (tid == 0) {
       graft::raise_flag(err, GRAFT_ERR_CAPACITY);
@@ -288,9 +308,9 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     s_nsrc[i] = c == 0 ? GRAFT_SRC_ROOT : GRAFT_SRC_DRAFT;
     s_low[i] = (c > 0 && s_score[c] < thresh) ? 1 : 0;
   }
-  for (int r = tid; r < R; r += kThreads) {
+  for (int r = tid; r < Rk; r += kThreads) {
     int tp = s_rpar[r];
-    int p = tp < 0 ? 0 : nd + tp;
+    int p = tp < 0 ? (tail ? nd - 1 : 0) : nd + tp;  // tail: under the deepest kept node
     if (tp >= r) {
       graft::raise_flag(err, GRAFT_ERR_PARENT);
       p = 0;
@@ -371,6 +391,27 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
   write_padding(r0 + n, r0 + rows, o_parent, o_token, o_depth, o_pos, o_mask, o_src);
 }
 
+// Graft-TAIL cut: per request, the number of leading block tokens with
+// confidence >= tau (NaN counts as below) and the token at the deepest kept
+// node, the retrieval root (the tree root when none is kept).
+__global__ __launch_bounds__(256) void tail_cut_kernel(int B, int L, const int32_t *__restrict__ root_token,
+                                                       const int32_t *__restrict__ block_token,
+                                                       const float *__restrict__ block_conf, float tau,
+                                                       int32_t *__restrict__ keep_len,
+                                                       int32_t *__restrict__ retrieval_root) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const float *conf = block_conf + static_cast<size_t>(b) * L;
+  int K = L;
+  for (int i = 0; i < L; ++i)
+    if (!(conf[i] >= tau)) {
+      K = i;
+      break;
+    }
+  keep_len[b] = K;
+  retrieval_root[b] = K == 0 ? root_token[b] : block_token[static_cast<size_t>(b) * L + K - 1];
+}
+
 }  // namespace
 
 extern "C" int graft_build_tree(int B, int mode, const int32_t *cand_parent, const int32_t *cand_token,
@@ -383,7 +424,7 @@ extern "C" int graft_build_tree(int B, int mode, const int32_t *cand_parent, con
                                 uint64_t *mask, int8_t *src, int32_t *err_flag, graft_stream stream) {
   using graft::fail;
   if (B < 0) return fail(GRAFT_EINVAL, "build_tree: B=%d", B);
-  if (mode != GRAFT_TREE_PRUNE && mode != GRAFT_TREE_STATIC_REPLACE)
+  if (mode != GRAFT_TREE_PRUNE && mode != GRAFT_TREE_STATIC_REPLACE && mode != GRAFT_TREE_TAIL)
     return fail(GRAFT_EINVAL, "build_tree: unknown mode %d", mode);
   if (V <= 0) return fail(GRAFT_EINVAL, "build_tree: V=%d", V);
   if (max_cand < 1 || max_cand > GRAFT_MAX_CAND)
@@ -392,7 +433,7 @@ extern "C" int graft_build_tree(int B, int mode, const int32_t *cand_parent, con
   if (!cand_parent || !cand_token || !cand_score || !cand_off || !budget || !ctx_len || !row_off ||
       !n_out || !parent || !token || !depth || !pos || !mask || !src)
     return fail(GRAFT_EINVAL, "build_tree: NULL array");
-  if (mode == GRAFT_TREE_PRUNE && ret_off && (!ret_token || !ret_parent))
+  if ((mode == GRAFT_TREE_PRUNE || mode == GRAFT_TREE_TAIL) && ret_off && (!ret_token || !ret_parent))
     return fail(GRAFT_EINVAL, "build_tree: ret_off given without ret_token/ret_parent");
   if (mode == GRAFT_TREE_STATIC_REPLACE && (!table || k < 1 || k > GRAFT_MAX_K))
     return fail(GRAFT_EINVAL, "build_tree: static replacement needs table and 1<=k<=%d", GRAFT_MAX_K);
@@ -402,4 +443,19 @@ extern "C" int graft_build_tree(int B, int mode, const int32_t *cand_parent, con
                      ret_parent, ret_off, table, V, k, replace_thresh, ctx_len, row_off, n_out, parent,
                      token, depth, pos, mask, src, err_flag);
   return graft::check_launch("build_tree");
+}
+
+extern "C" int graft_tail_cut(int B, int L, const int32_t *root_token, const int32_t *block_token,
+                              const float *block_conf, float tau, int32_t *keep_len, int32_t *retrieval_root,
+                              graft_stream stream) {
+  using graft::fail;
+  if (B < 0 || L < 1 || L >= GRAFT_MAX_NODES) return fail(GRAFT_EINVAL, "tail_cut: B=%d L=%d (1..%d)", B, L,
+                                                           GRAFT_MAX_NODES - 1);
+  if (B == 0) return GRAFT_OK;
+  if (!root_token || !block_token || !block_conf || !keep_len || !retrieval_root)
+    return fail(GRAFT_EINVAL, "tail_cut: NULL array");
+  graft::clear_error();
+  hipLaunchKernelGGL(tail_cut_kernel, dim3((B + 255) / 256), dim3(256), 0, graft::as_stream(stream), B, L, root_token,
+                     block_token, block_conf, tau, keep_len, retrieval_root);
+  return graft::check_launch("tail_cut");
 }

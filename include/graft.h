@@ -88,6 +88,8 @@ typedef void *graft_stream;
 #define GRAFT_TREE_PRUNE 0          /* top-budget draft nodes + retrieved nodes */
 #define GRAFT_TREE_STATIC_REPLACE 1 /* top-budget draft nodes, low-score ones
                                        swapped for table successors */
+#define GRAFT_TREE_TAIL 2           /* block draft: confident prefix kept, the
+                                       freed slots from retrieval under it */
 
 const char *graft_last_error(void);
 int graft_version(void);
@@ -151,6 +153,16 @@ int graft_table_update_retrieve(int32_t *table, int V, int k,
  *   child of its parent takes token table[token(parent)][j] when j < k
  *   (parent token after its own replacement), source GRAFT_SRC_REPLACED.
  *   table (device int32 [V, k]) is read only in this mode.
+ * mode GRAFT_TREE_TAIL (Graft page, section 7, Graft-TAIL on block drafts;
+ *   the thresholds and shapes are this library's reading): the candidates
+ *   are the root and a block draft, cand_score = the drafter's confidence
+ *   per token; candidates 0..K are kept, where K + 1 is the first index
+ *   >= 1 with cand_score < replace_thresh (NaN counts as below), and the
+ *   first budget[b] - (K + 1) retrieved rows of the request follow, their
+ *   template parent -1 meaning node K (the deepest kept node).  The rows
+ *   must be a template whose first rows are the smaller templates (as
+ *   graft_make_template's are), expanded from graft_tail_cut's
+ *   retrieval_root.  budget[b] = 1 + block length keeps the slot count.
  * Output per request (device, padded row layout given by row_off [B+1]):
  *   n_out[b]; parent, token, depth, pos = ctx_len[b] + depth (int32),
  *   mask (uint64: bit j set iff node j is the node or its ancestor) and
@@ -169,6 +181,19 @@ int graft_build_tree(int B, int mode,
                      int32_t *n_out, int32_t *parent, int32_t *token, int32_t *depth,
                      int32_t *pos, uint64_t *mask, int8_t *src, int32_t *err_flag,
                      graft_stream stream);
+
+/*
+ * Graft-TAIL cut (Graft page, section 7): per request b, keep_len[b] = the
+ * number of leading block tokens with confidence >= tau (NaN counts as
+ * below) and retrieval_root[b] = the token of the deepest kept node, i.e.
+ * block_token[b * L + keep_len[b] - 1], or root_token[b] when none is kept:
+ * the root to pass to graft_table_update_retrieve before graft_build_tree
+ * in mode GRAFT_TREE_TAIL.  block_token [B, L], block_conf [B, L] (fp32),
+ * root_token [B], outputs [B]: device.  1 <= L <= 63.
+ */
+int graft_tail_cut(int B, int L, const int32_t *root_token, const int32_t *block_token,
+                   const float *block_conf, float tau, int32_t *keep_len, int32_t *retrieval_root,
+                   graft_stream stream);
 
 /*
  * Tree-masked grouped-query attention (Graft page, section 2, third step:

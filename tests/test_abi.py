@@ -174,3 +174,17 @@ def test_sampling_host_validation_launches_nothing(native):
     assert L.graft_accept_sampled(-1, p, p, p, p, p, p, p, p, None, None) == E
     assert L.graft_accept_sampled(2, p, p, p, p, None, p, p, p, None, None) == E
     assert L.graft_accept_sampled(0, None, None, None, None, None, None, None, None, None, None) == 0
+
+
+def test_tail_host_validation_launches_nothing(native):
+    L = native.lib()
+    E = native.GRAFT_EINVAL
+    p = 1
+    assert L.graft_tail_cut(4, 0, p, p, p, 0.5, p, p, None) == E      # empty block
+    assert L.graft_tail_cut(4, 64, p, p, p, 0.5, p, p, None) == E     # tree of 65 nodes
+    assert L.graft_tail_cut(4, 16, p, p, None, 0.5, p, p, None) == E
+    assert L.graft_tail_cut(0, 16, None, None, None, 0.5, None, None, None) == 0
+    # build_tree accepts the tail mode (and still rejects unknown ones)
+    args = [p, p, p, p, 17, p, None, None, None, None, 1000, 8, 0.5, p, p, p, p, p, p, p, p, p, None, None]
+    assert L.graft_build_tree(0, 2, *args) == 0
+    assert L.graft_build_tree(1, 3, *args) == E

@@ -7,6 +7,7 @@ from oracle import OracleError
 from oracle import accept as OAcc
 from oracle import kv as OKV
 from oracle import sample as OS
+from oracle import tail as OTail
 from oracle import attention as OA
 from oracle import lmhead as OL
 from oracle import table as OTab
@@ -666,6 +667,55 @@ def test_build_static_replace_matches_oracle(api):
     for key in ("n", "parent", "token", "depth", "pos", "mask", "src"):
         assert np.array_equal(got[key], exp[key]), key
     assert (got["src"] == 3).sum() > 100
+
+
+# ----------------------------------------------------------------------------- Graft-TAIL
+
+def test_tail_cut_retrieve_build_match_oracle(api):
+    """Graft-TAIL through the C ABI: graft_tail_cut, retrieval from its roots,
+    graft_build_tree in tail mode, against the oracle (cuts at 0, in the
+    middle, at L; a NaN confidence; ragged row capacities)."""
+    r = np.random.default_rng(1616)
+    V, k, L, tau = 500, 8, 16, 0.5
+    table = np.stack([r.choice(V, k, replace=False) for _ in range(V)]).astype(np.int32)
+    B = 12
+    block = r.integers(0, V, (B, L)).astype(np.int32)
+    conf = r.random((B, L)).astype(np.float32) * 0.5 + 0.5   # all >= tau ...
+    for b in range(B):
+        cut = [0, 3, 16, 7, 1, 15, 9, 16, 0, 5, 12, 2][b]
+        if cut < L:
+            conf[b, cut] = np.float32(0.2)                   # ... up to the cut
+    conf[4, 1] = np.nan                                      # NaN is below tau
+    roots = r.integers(0, V, B).astype(np.int32)
+    ctx = r.integers(0, 9000, B).astype(np.int32)
+    keep = torch.empty(B, dtype=torch.int32, device="cuda")
+    rroot = torch.empty(B, dtype=torch.int32, device="cuda")
+    api.graft_tail_cut(dev_i32(roots), dev_i32(block), torch.from_numpy(conf).cuda(), tau, keep, rroot)
+    torch.cuda.synchronize()
+    exp_keep = [OTail.keep_length(conf[b], tau) for b in range(B)]
+    exp_root = [OTail.retrieval_root(int(roots[b]), block[b], conf[b], tau) for b in range(B)]
+    assert keep.cpu().numpy().tolist() == exp_keep
+    assert rroot.cpu().numpy().tolist() == exp_root
+    tp, tr, _ = otemplate(L, k, 8)
+    tps = np.tile(np.array(tp, np.int32), B)
+    trs = np.tile(np.array(tr, np.int32), B)
+    toff = (np.arange(B + 1) * L).astype(np.int32)
+    _, got_r, err = _table_gpu(api, table, np.array([0]), np.array([0, 1]), np.array([5], np.int32),
+                               np.zeros((1, k), np.int32), rroot.cpu().numpy(), tps, trs, toff)
+    assert err == 0
+    cands, rets, caps = [], [], []
+    for b in range(B):
+        cands.append((np.arange(-1, L, dtype=np.int32), np.concatenate([[roots[b]], block[b]]).astype(np.int32),
+                      np.concatenate([[1.0], conf[b]]).astype(np.float32)))
+        rets.append((got_r[b * L:(b + 1) * L], np.array(tp, np.int32)))
+        caps.append(1 + L + b % 3)
+    got, row_off, err = _build_gpu(api, 2, cands, [1 + L] * B, rets, ctx, caps, V=V, thresh=tau)
+    assert err == 0
+    ret_o = np.concatenate([OTab.retrieve(table, exp_root[b], tp, tr) for b in range(B)]).astype(np.int32)
+    exp = OTail.build_batch(roots, block, conf, tau, ret_o, tps, toff, ctx, V, row_off)
+    assert np.array_equal(got_r, ret_o)
+    for key in ("n", "parent", "token", "depth", "pos", "mask", "src"):
+        assert np.array_equal(got[key], exp[key]), key
 
 
 # ----------------------------------------------------------------------------- KV compaction
