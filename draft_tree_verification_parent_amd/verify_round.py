@@ -26,7 +26,7 @@ import numpy as np
 import torch
 
 from . import api
-from ._native import TREE_PRUNE, TREE_STATIC_REPLACE, W_PACKED, W_ROWMAJOR
+from ._native import TREE_PRUNE, TREE_STATIC_REPLACE, TREE_TAIL, W_PACKED, W_ROWMAJOR
 
 STEPS_FUSED = ("update_retrieve", "build_tree", "tree_attention", "lmhead_topk", "accept")
 STEPS_SPLIT = ("update_retrieve", "build_tree", "tree_attention", "lmhead", "topk", "accept")
@@ -63,7 +63,8 @@ class VerifyRound:
             base = STEPS_FUSED_T if fused else STEPS_SPLIT_T
         else:
             base = STEPS_FUSED if fused else STEPS_SPLIT
-        self.steps = base + (("kv_compact",) if chain else ())
+        self.tail = bool(getattr(ri.wl, "tail", False))
+        self.steps = (("tail_cut",) if self.tail else ()) + base + (("kv_compact",) if chain else ())
         wl = ri.wl
         self.ri, self.wl, self.dev = ri, wl, dev
         B, N, k, V = ri.B, ri.N, ri.k, ri.V
@@ -95,7 +96,16 @@ class VerifyRound:
         self.max_ctx = int(ri.kv_cap - ri.N) if chain else int(np.max(ri.ctx_len))
         self.row_off = _i32(ri.row_off, dev)
         self.root_token = _i32(ri.root_token, dev)
-        self.mode = TREE_STATIC_REPLACE if wl.static_replace else TREE_PRUNE
+        self.mode = TREE_TAIL if self.tail else (TREE_STATIC_REPLACE if wl.static_replace else TREE_PRUNE)
+        if self.tail:
+            # Graft-TAIL: the block after each root and its confidences, and
+            # the cut's outputs (kept length, retrieval root)
+            L = N - 1
+            idx = np.asarray(ri.cand_off[:-1], np.int64)[:, None] + 1 + np.arange(L)[None, :]
+            self.block_token = _i32(np.asarray(ri.cand_token)[idx], dev)
+            self.block_conf = torch.from_numpy(np.ascontiguousarray(np.asarray(ri.cand_score)[idx], np.float32)).to(dev)
+            self.tail_keep = torch.empty(B, dtype=torch.int32, device=dev)
+            self.tail_root = torch.empty(B, dtype=torch.int32, device=dev)
 
         # the update list of the first round: the synthetic previous round
         self.upd = dict(n=_i32(ri.prev_n, dev), row_off=_i32(ri.prev_row_off, dev),
@@ -175,10 +185,15 @@ class VerifyRound:
                         rows=self.rows)
 
     # individual steps -------------------------------------------------
+    def step_tail_cut(self):
+        api.graft_tail_cut(self.root_token, self.block_token, self.block_conf, self.wl.replace_thresh,
+                           self.tail_keep, self.tail_root)
+
     def step_update_retrieve(self):
         u = self.upd
+        root = self.tail_root if self.tail else self.root_token  # Graft-TAIL: the deepest kept node
         api.graft_table_update_retrieve(self.table, u["n"], u["row_off"], u["rows"], u["token"],
-                                        u["topk"], self.root_token, self.tmpl_parent, self.tmpl_rank,
+                                        u["topk"], root, self.tmpl_parent, self.tmpl_rank,
                                         self.tmpl_off, self.tmpl_rows, self.ret_token, self.err)
 
     def step_build_tree(self):

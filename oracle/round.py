@@ -22,6 +22,7 @@ from . import attention as _attention
 from . import kv as _kv
 from . import lmhead as _lmhead
 from . import table as _table
+from . import tail as _tail
 from . import template as _template
 from . import topk as _topk
 from . import tree as _tree
@@ -31,6 +32,8 @@ def tree_stage(ri, dmax: int = 8):
     """Update + retrieve + build.  Returns dict(table, tparent, trank,
     tmpl_off, ret_token, tree)."""
     table = _table.update(ri.table, ri.prev_n, ri.prev_row_off, ri.prev_token, ri.prev_topk)
+    if getattr(ri.wl, "tail", False):
+        return _tail_tree_stage(ri, table, dmax)
     tp_all, tr_all, rt_all, off = [], [], [], [0]
     for b in range(ri.B):
         tp, tr, _ = _template.template(int(ri.n_ret[b]), ri.k, dmax)
@@ -50,6 +53,30 @@ def tree_stage(ri, dmax: int = 8):
                              replace_thresh=wl.replace_thresh)
     return dict(table=table, tparent=tparent, trank=trank, tmpl_off=tmpl_off,
                 ret_token=ret_token, tree=tree)
+
+
+def _tail_tree_stage(ri, table, dmax: int):
+    """Graft-TAIL workloads: candidates are the root and a block of L tokens
+    (cand_score = confidences); retrieval runs from each request's deepest
+    kept node with the size-L template (oracle.tail)."""
+    L = ri.N - 1
+    tau = ri.wl.replace_thresh
+    tp, tr, _ = _template.template(L, ri.k, dmax)
+    roots, blocks, confs, rets, rroots = [], [], [], [], []
+    for b in range(ri.B):
+        o = int(ri.cand_off[b])
+        roots.append(int(ri.cand_token[o]))
+        blocks.append(np.asarray(ri.cand_token[o + 1:o + 1 + L], np.int32))
+        confs.append(np.asarray(ri.cand_score[o + 1:o + 1 + L], np.float32))
+        rroots.append(_tail.retrieval_root(roots[-1], blocks[-1], confs[-1], tau))
+        rets += _table.retrieve(table, rroots[-1], tp, tr)
+    tparent = np.tile(np.array(tp, np.int32), ri.B)
+    trank = np.tile(np.array(tr, np.int32), ri.B)
+    tmpl_off = (np.arange(ri.B + 1) * L).astype(np.int32)
+    ret_token = np.array(rets, np.int32)
+    tree = _tail.build_batch(roots, blocks, confs, tau, ret_token, tparent, tmpl_off, ri.ctx_len, ri.V, ri.row_off)
+    return dict(table=table, tparent=tparent, trank=trank, tmpl_off=tmpl_off, ret_token=ret_token, tree=tree,
+                retrieval_root=np.array(rroots, np.int32))
 
 
 def kv_f64(ri, b: int):

@@ -57,6 +57,7 @@ class Workload:
     D: int = 5        # drafter depth
     Wf: int = 10      # drafter frontier width
     m: int = 10       # children per frontier node
+    tail: bool = False  # Graft-TAIL on a block draft of n_nodes - 1 tokens
 
     def with_ctx(self, lo: int, hi: int | None = None) -> "Workload":
         d = dict(self.__dict__)
@@ -91,6 +92,10 @@ WORKLOADS = {
                 B=16, Hq=32, Hkv=8, d=128, H=4096, V=151936, k=8, ctx_lo=4096, ctx_hi=16384,
                 tree="eagle", n_nodes=60, draft_budget=60, n_retrieved=0,
                 static_replace=True, replace_thresh=0.05),
+    6: Workload(6, "Graft-TAIL on DFlash-style block drafts: 4 requests, Qwen3-8B shapes, ctx 4096, 16-token blocks "
+                   "cut at confidence < 0.5, tails from a shared 151936x8 table",
+                B=4, Hq=32, Hkv=8, d=128, H=4096, V=151936, k=8, ctx_lo=4096, ctx_hi=4096,
+                tree="block", n_nodes=17, draft_budget=17, n_retrieved=16, tail=True, replace_thresh=0.5),
 }
 
 
@@ -140,6 +145,19 @@ def eagle_candidates(r: np.random.Generator, V: int, D: int, Wf: int, m: int, ro
                 newest.append(len(parent) - 1)
     return (np.array(parent, np.int32), np.array(token, np.int32),
             np.array(score, np.float64).astype(np.float32))
+
+
+def block_draft(r: np.random.Generator, V: int, L: int, root_token: int):
+    """A stand-in for a block (diffusion) drafter: the root and L chained
+    tokens (Zipf over the vocabulary) with per-token confidences that decay
+    along the block, conf_i = prod_{j<=i} b_j, b_j ~ Beta(8, 1) -- the score
+    Graft-TAIL cuts on."""
+    cdf = _zipf_cdf(V)
+    tokens = np.concatenate([[root_token], zipf_ids(r, cdf, L)]).astype(np.int32)
+    conf = np.cumprod(r.beta(8.0, 1.0, L)).astype(np.float32)
+    parent = np.arange(-1, L, dtype=np.int32)
+    score = np.concatenate([[1.0], conf]).astype(np.float32)
+    return parent, tokens, score
 
 
 def random_tree(r: np.random.Generator, V: int, N: int, root_token: int,
@@ -288,6 +306,8 @@ def make_round_inputs(wl: Workload, kv: bool = True, extra_slots: int = 0) -> Ro
         root = int(ctx_tok[-1]) if ctx_tok is not None else int(rb.integers(0, V))
         if wl.tree == "random":
             p, t, s = random_tree(rb, V, N, root)
+        elif wl.tree == "block":
+            p, t, s = block_draft(rb, V, N - 1, root)
         else:
             p, t, s = eagle_candidates(rb, V, wl.D, wl.Wf, wl.m, root)
         cp.append(p); ct.append(t); cs.append(s)

@@ -37,10 +37,10 @@ def _sample_nodes(rng, n, per_request):
     return nodes
 
 
-ATTN_SAMPLES = {1: 99, 2: 99, 3: 12, 4: 6, 5: 2}
+ATTN_SAMPLES = {1: 99, 2: 99, 3: 12, 4: 6, 5: 2, 6: 8}
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
 def test_round_parity(cfg):
     _need_gpu()
     wl, ri, w, ts, hidden, vr = run_gpu_round(cfg)
@@ -94,7 +94,7 @@ def test_round_parity(cfg):
 
     # top-k: exact on sampled rows; argmax property on every row
     rows = np.arange(logits.shape[0]) if logits.shape[0] <= 64 else np.sort(
-        rng.choice(logits.shape[0], 96, replace=False))
+        rng.choice(logits.shape[0], min(96, logits.shape[0]), replace=False))
     ids, vals = OT.topk(logits[rows], ri.k)
     assert np.array_equal(topk_id[rows], ids)
     assert np.array_equal(topk_val[rows], vals)
@@ -193,7 +193,7 @@ def test_graph_replay_matches_eager(cfg, per_graph):
     say(f"[graph] cfg {cfg}: 4 replays of {per_graph} round(s) identical to eager rounds")
 
 
-@pytest.mark.parametrize("cfg,T", [(2, 0.0), (5, 0.0), (2, 1.0)])
+@pytest.mark.parametrize("cfg,T", [(2, 0.0), (5, 0.0), (2, 1.0), (6, 0.0)])
 def test_chained_rounds_match_oracle(cfg, T):
     """Three rounds chained on the GPU (KV compaction, context advance, bonus
     token as the next root) against the oracle's chain, round by round: the
