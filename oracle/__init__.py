@@ -33,6 +33,8 @@ Modules:
   accept     -- greedy acceptance: deepest accepted node, path, bonus token
   sample     -- acceptance at temperature T > 0: Gumbel-max draws per node,
                 first matching child (a reading: the pages give no rule)
+  treegraft  -- TreeGraft's shared tree from a small and a mid drafter
+                (extended pool, non-destructive graft) before the prune
   tail       -- Graft-TAIL: a block draft's confident prefix kept, its tail
                 replaced by retrieval under the deepest kept node
   kv         -- KV compaction to the accepted path and round chaining
