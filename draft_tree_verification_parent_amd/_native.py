@@ -33,6 +33,8 @@ SIGNATURES = {
     "graft_lmhead_topk_sample": (c_int, [c_int, c_int, c_int, c_int, c_float, P, P, P, P, P, P, P, c_size_t, P]),
     "graft_sample_rows": (c_int, [c_int, c_int, c_float, P, P, P, P]),
     "graft_accept_sampled": (c_int, [c_int, P, P, P, P, P, P, P, P, P, P]),
+    "graft_treegraft_node_count": (c_int, [c_int, c_int, c_int, c_int]),
+    "graft_treegraft_build": (c_int, [c_int, c_int, c_int, c_int, P, P, P, P, P, P, P, P, P, P, P]),
     "graft_tail_cut": (c_int, [c_int, c_int, P, P, P, c_float, P, P, P]),
     "graft_kv_compact": (c_int, [c_int, c_int, c_int, c_int, P, P, c_int64, P, c_int64, P, P, P, P, P, P, P, P,
                                  P]),

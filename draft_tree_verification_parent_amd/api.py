@@ -150,6 +150,21 @@ def graft_accept_sampled(n, row_off, parent, token, sample_id, acc_len, acc_path
                 _p(err, "i32", "err"), _s(stream))
 
 
+def graft_treegraft_node_count(D, W, m, mid_mask):
+    return int(N.lib().graft_treegraft_node_count(int(D), int(W), int(m), int(mid_mask)))
+
+
+def graft_treegraft_build(D, W, m, mid_mask, root_token, tok, prob, q, cand_off, cand_parent, cand_token, cand_score,
+                          err=None, stream=None):
+    """TreeGraft's shared tree per request (see include/graft.h)."""
+    B = root_token.numel()
+    return call("graft_treegraft_build", int(B), int(D), int(W), int(m), _p(mid_mask, "i32", "mid_mask"),
+                _p(root_token, "i32", "root_token"), _p(tok, "i32", "tok"), _p(prob, "f32", "prob"),
+                _p(q, "f32", "q"), _p(cand_off, "i32", "cand_off"), _p(cand_parent, "i32", "cand_parent"),
+                _p(cand_token, "i32", "cand_token"), _p(cand_score, "f32", "cand_score"), _p(err, "i32", "err"),
+                _s(stream))
+
+
 def graft_tail_cut(root_token, block_token, block_conf, tau, keep_len, retrieval_root, stream=None):
     """Graft-TAIL: per request the kept prefix length of a block draft and
     the retrieval root (token of the deepest kept node)."""

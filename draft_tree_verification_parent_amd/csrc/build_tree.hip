@@ -128,6 +128,32 @@ __device__ inline uint64_t top64_merge(uint64_t a, uint64_t b, int lane, bool de
   return bitonic_step<64, 1>(x, lane, desc);
 }
 
+// The 64 largest keys of a 512-thread workgroup (thread tid holds the key of
+// item p * 512 + tid in kreg[p]; NB = number of 64-item blocks in use),
+// sorted descending, in the lanes of wavefront 0 (other wavefronts: partial
+// results).  Each wavefront sorts its blocks in registers and keeps the top
+// 64; three rounds of pairwise merges through LDS follow, partners sorted in
+// opposite directions.  Every thread must call it (three barriers).
+__device__ inline uint64_t workgroup_top64(const uint64_t (&kreg)[kPasses], int NB, int wave, int lane,
+                                           uint64_t (*s_m1)[64], uint64_t (*s_m2)[64], uint64_t *s_m3) {
+  const bool dir0 = (wave & 1) == 0;
+  uint64_t top = wave_sort(kreg[0], lane, dir0);
+#pragma unroll
+  for (int pass = 1; pass < kPasses; ++pass)
+    if (pass * kWavesBT < NB)  // uniform
+      top = top64_merge(top, wave_sort(kreg[pass], lane, !dir0), lane, dir0);
+  if (wave & 1) s_m1[wave >> 1][lane] = top;
+  __syncthreads();
+  if (!(wave & 1)) top = top64_merge(top, s_m1[wave >> 1][lane], lane, ((wave >> 1) & 1) == 0);
+  if ((wave & 3) == 2) s_m2[wave >> 2][lane] = top;
+  __syncthreads();
+  if ((wave & 3) == 0) top = top64_merge(top, s_m2[wave >> 2][lane], lane, ((wave >> 2) & 1) == 0);
+  if (wave == 4) s_m3[lane] = top;
+  __syncthreads();
+  if (wave == 0) top = top64_merge(top, s_m3[lane], lane, true);
+  return top;
+}
+
 __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     int mode, const int32_t *__restrict__ cand_parent, const int32_t *__restrict__ cand_token,
     const float *__restrict__ cand_score, const int32_t *__restrict__ cand_off, int max_cand,
@@ -213,24 +239,9 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
   // of its keys; three rounds of pairwise merges across wavefronts leave the
   // 64 largest keys of the request in wavefront 0, where entry bud-2 is the
   // smallest key kept.  Merge partners are sorted in opposite directions.
-  const int NB = (C + 63) / 64;
-  const bool dir0 = (wave & 1) == 0;
-  uint64_t top = wave_sort(kreg[0], lane64, dir0);
-#pragma unroll
-  for (int pass = 1; pass < kPasses; ++pass)
-    if (pass * kWavesBT < NB)  // uniform
-      top = top64_merge(top, wave_sort(kreg[pass], lane64, !dir0), lane64, dir0);
-  if (wave & 1) s_m1[wave >> 1][lane64] = top;
-  __syncthreads();
-  if (!(wave & 1)) top = top64_merge(top, s_m1[wave >> 1][lane64], lane64, ((wave >> 1) & 1) == 0);
-  if ((wave & 3) == 2) s_m2[wave >> 2][lane64] = top;
-  __syncthreads();
-  if ((wave & 3) == 0) top = top64_merge(top, s_m2[wave >> 2][lane64], lane64, ((wave >> 2) & 1) == 0);
-  if (wave == 4) s_m3[lane64] = top;
-  __syncthreads();
+  const uint64_t top = workgroup_top64(kreg, (C + 63) / 64, wave, lane64, s_m1, s_m2, s_m3);
   const int need = bud - 1;
   if (wave == 0) {
-    top = top64_merge(top, s_m3[lane64], lane64, true);
     // need > 64 keeps the 64 largest, already more than a request can hold
     const int at = need <= 0 ? 0 : (need < 64 ? need - 1 : 63);
     if (lane64 == at) s_thr = need <= 0 ? ~0ull : top;
@@ -391,6 +402,118 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
   write_padding(r0 + n, r0 + rows, o_parent, o_token, o_depth, o_pos, o_mask, o_src);
 }
 
+// Nodes TreeGraft's construction creates (root included): sizes and the
+// schedule decide it, not the data.  -1 if a step would exceed max_nodes.
+__host__ __device__ inline int treegraft_count(int D, int W, int m, int mid_mask, int max_nodes) {
+  int n = 1, newest = 1, visited = 0;
+  for (int k = 0; k < D; ++k) {
+    const bool mid = (mid_mask >> k) & 1;
+    const int pool = mid ? n - visited : newest;
+    const int f = pool < W ? pool : W;
+    if (mid) visited = n;
+    newest = f * m;
+    n += newest;
+    if (n > max_nodes) return -1;
+  }
+  return n;
+}
+
+// TreeGraft's shared tree (TreeGraft page, section 3: frontier = best W of
+// the pool by cumulative score, m children each; section 4 "Where"/"How": a
+// mid-drafter step's pool is every node it has not visited, ranked by its own
+// path score; children are appended, never overwriting).  One 512-thread
+// workgroup per request; per step the pool's keys (score order << 11 |
+// 2047 - node) go through the workgroup top-64, wavefront 0 writes the W
+// best to LDS, then every child is created by one thread.  Stored score s and
+// mid score r are fp32 products, as the oracle forms them.
+__global__ __launch_bounds__(kThreads) void treegraft_kernel(int D, int W, int m, const int32_t *__restrict__ mid_mask,
+                                                             const int32_t *__restrict__ root_token,
+                                                             const int32_t *__restrict__ tok,
+                                                             const float *__restrict__ prob,
+                                                             const float *__restrict__ q,
+                                                             const int32_t *__restrict__ cand_off,
+                                                             int32_t *__restrict__ out_parent,
+                                                             int32_t *__restrict__ out_token,
+                                                             float *__restrict__ out_score, int32_t *__restrict__ err) {
+  __shared__ float s_s[GRAFT_MAX_CAND];
+  __shared__ float s_r[GRAFT_MAX_CAND];
+  __shared__ signed char s_created[GRAFT_MAX_CAND];
+  __shared__ signed char s_visited[GRAFT_MAX_CAND];
+  __shared__ uint64_t s_m1[4][64], s_m2[2][64], s_m3[64];
+  __shared__ int s_front[64];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int mask = mid_mask[b];
+  const int base = cand_off[b];
+  const int cap = cand_off[b + 1] - base;
+  const int total = treegraft_count(D, W, m, mask, GRAFT_MAX_CAND);
+  if (total < 0 || total != cap) {
+    if (tid == 0) graft::raise_flag(err, GRAFT_ERR_CAPACITY);
+    return;
+  }
+  const size_t step_stride = static_cast<size_t>(W) * m;
+  const int32_t *tok_b = tok + static_cast<size_t>(b) * D * step_stride;
+  const float *prob_b = prob + static_cast<size_t>(b) * D * step_stride;
+  if (tid == 0) {
+    s_s[0] = 1.f;
+    s_r[0] = 1.f;
+    s_created[0] = 0;
+    s_visited[0] = 0;
+    out_parent[base] = -1;
+    out_token[base] = root_token[b];
+    out_score[base] = 1.f;
+  }
+  __syncthreads();
+  int n = 1, newest = 1, visited = 0;
+  for (int k = 0; k < D; ++k) {
+    const bool mid = (mask >> k) & 1;
+    const int pool = mid ? n - visited : newest;
+    const int F = pool < W ? pool : W;
+    uint64_t kreg[kPasses];
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const int v = pass * kThreads + tid;
+      uint64_t key = 0;
+      if (v < n) {
+        const bool in_pool = mid ? !s_visited[v] : s_created[v] == k;
+        if (in_pool)
+          key = (1ull << 43) | (static_cast<uint64_t>(graft::float_order(mid ? s_r[v] : s_s[v])) << 11) |
+                static_cast<uint64_t>(2047 - v);
+      }
+      kreg[pass] = key;
+    }
+    const uint64_t top = workgroup_top64(kreg, (n + 63) / 64, wave, lane, s_m1, s_m2, s_m3);
+    if (wave == 0 && lane < F) s_front[lane] = 2047 - static_cast<int>(top & 2047);
+    if (mid) {
+#pragma unroll
+      for (int pass = 0; pass < kPasses; ++pass)
+        if (kreg[pass] != 0) s_visited[pass * kThreads + tid] = 1;  // the pool is visited now
+    }
+    __syncthreads();
+    for (int t = tid; t < F * m; t += kThreads) {
+      const int j = t / m, c = t - j * m;
+      const int f = s_front[j];
+      const int v = n + t;
+      const size_t o = static_cast<size_t>(k) * step_stride + static_cast<size_t>(j) * m + c;
+      const float sv = s_s[f] * prob_b[o];
+      const float rv = s_r[f] * q[base + v];
+      s_s[v] = sv;
+      s_r[v] = rv;
+      s_created[v] = static_cast<signed char>(k + 1);
+      s_visited[v] = 0;
+      out_parent[base + v] = f;
+      out_token[base + v] = tok_b[o];
+      out_score[base + v] = sv;
+    }
+    __syncthreads();
+    if (mid) visited = n;
+    newest = F * m;
+    n += newest;
+  }
+}
+
 // Graft-TAIL cut: per request, the number of leading block tokens with
 // confidence >= tau (NaN counts as below) and the token at the deepest kept
 // node, the retrieval root (the tree root when none is kept).
@@ -458,4 +581,26 @@ extern "C" int graft_tail_cut(int B, int L, const int32_t *root_token, const int
   hipLaunchKernelGGL(tail_cut_kernel, dim3((B + 255) / 256), dim3(256), 0, graft::as_stream(stream), B, L, root_token,
                      block_token, block_conf, tau, keep_len, retrieval_root);
   return graft::check_launch("tail_cut");
+}
+
+extern "C" int graft_treegraft_node_count(int D, int W, int m, int mid_mask) {
+  if (D < 0 || W < 1 || W > 64 || m < 1) return -1;
+  return treegraft_count(D, W, m, mid_mask, GRAFT_MAX_CAND);
+}
+
+extern "C" int graft_treegraft_build(int B, int D, int W, int m, const int32_t *mid_mask, const int32_t *root_token,
+                                     const int32_t *tok, const float *prob, const float *q, const int32_t *cand_off,
+                                     int32_t *cand_parent, int32_t *cand_token, float *cand_score, int32_t *err_flag,
+                                     graft_stream stream) {
+  using graft::fail;
+  if (B < 0 || D < 0 || D > 30 || W < 1 || W > 64 || m < 1 || m > GRAFT_MAX_CAND)
+    return fail(GRAFT_EINVAL, "treegraft_build: B=%d D=%d W=%d (1..64) m=%d", B, D, W, m);
+  if (B == 0) return GRAFT_OK;
+  if (!mid_mask || !root_token || !cand_off || !cand_parent || !cand_token || !cand_score || !q ||
+      (D > 0 && (!tok || !prob)))
+    return fail(GRAFT_EINVAL, "treegraft_build: NULL array");
+  graft::clear_error();
+  hipLaunchKernelGGL(treegraft_kernel, dim3(B), dim3(kThreads), 0, graft::as_stream(stream), D, W, m, mid_mask,
+                     root_token, tok, prob, q, cand_off, cand_parent, cand_token, cand_score, err_flag);
+  return graft::check_launch("treegraft_build");
 }

@@ -16,6 +16,8 @@
  *   graft_lmhead_topk_sample,    (temperature T > 0) one draw per row by
  *   graft_accept_sampled         Gumbel-max with the noise as an input, and
  *                                acceptance of the first matching child
+ *   graft_treegraft_build        (TreeGraft) the shared tree of a small and a
+ *                                mid drafter, upstream of graft_build_tree
  *   graft_kv_compact             (round chaining) the accepted path's K/V
  *                                moves to the front of the tree slots, the
  *                                context advances, the bonus becomes the
@@ -181,6 +183,39 @@ int graft_build_tree(int B, int mode,
                      int32_t *n_out, int32_t *parent, int32_t *token, int32_t *depth,
                      int32_t *pos, uint64_t *mask, int8_t *src, int32_t *err_flag,
                      graft_stream stream);
+
+/*
+ * TreeGraft's shared draft tree from a small and a mid drafter (TreeGraft
+ * page, section 3: at step k the frontier is the best W nodes of the pool by
+ * cumulative score s, the product of edge scores from the root, and each
+ * frontier node gets m children; section 4 "Where": a mid-drafter step's
+ * pool is every node it has not yet visited, ranked by its own path score,
+ * and visits the pool; a small-drafter step's pool is the previous step's
+ * new nodes with their stored scores; "How": children are appended without
+ * overwriting; the global prune to Bver is graft_build_tree afterwards).
+ * The drafters and the schedule ("When") are out of scope and come in:
+ *   mid_mask[b] (device int32): bit k set = step k is a mid-drafter step;
+ *   tok, prob (device [B][D][W][m], int32 / fp32): the step's drafter output
+ *     for the j-th best frontier node, child c (children are created in that
+ *     order, numbered after every earlier node);
+ *   q (device fp32, the candidate layout): q[cand_off[b] + v] is the mid
+ *     drafter's probability of the edge into node v; its path score is
+ *     r(v) = fl(r(parent) * q[v]), r(root) = 1.
+ * A child of frontier node f gets score fl(s(f) * prob); ties in ranking go
+ * to the lower node index.  Output per request at cand_off[b] (device
+ * [B+1]): cand_parent (root -1), cand_token (root = root_token[b]),
+ * cand_score = s, in creation order (topological): the candidate arrays of
+ * graft_build_tree.  cand_off[b+1] - cand_off[b] must equal
+ * graft_treegraft_node_count(D, W, m, mid_mask[b]) (a host helper: the
+ * count depends on the sizes and schedule only; -1 for invalid sizes or
+ * more than GRAFT_MAX_CAND nodes), else the request is flagged ERR_CAPACITY
+ * and left unwritten.  1 <= W <= 64, D <= 30.
+ */
+int graft_treegraft_node_count(int D, int W, int m, int mid_mask);
+int graft_treegraft_build(int B, int D, int W, int m, const int32_t *mid_mask, const int32_t *root_token,
+                          const int32_t *tok, const float *prob, const float *q, const int32_t *cand_off,
+                          int32_t *cand_parent, int32_t *cand_token, float *cand_score, int32_t *err_flag,
+                          graft_stream stream);
 
 /*
  * Graft-TAIL cut (Graft page, section 7): per request b, keep_len[b] = the

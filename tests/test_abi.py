@@ -188,3 +188,18 @@ def test_tail_host_validation_launches_nothing(native):
     args = [p, p, p, p, 17, p, None, None, None, None, 1000, 8, 0.5, p, p, p, p, p, p, p, p, p, None, None]
     assert L.graft_build_tree(0, 2, *args) == 0
     assert L.graft_build_tree(1, 3, *args) == E
+
+
+def test_treegraft_host_helper_and_validation(native):
+    from oracle import treegraft as OTG
+    L = native.lib()
+    E = native.GRAFT_EINVAL
+    for D, W, m in [(5, 10, 10), (3, 4, 7), (0, 1, 1), (6, 64, 2)]:
+        for mask in (0, 1, 0b10101, (1 << D) - 1):
+            assert L.graft_treegraft_node_count(D, W, m, mask) == OTG.node_count(D, W, m, mask)
+    assert L.graft_treegraft_node_count(5, 65, 10, 0) == -1       # W > 64
+    assert L.graft_treegraft_node_count(5, 64, 64, 0) == -1       # more than 2048 nodes
+    p = 1
+    assert L.graft_treegraft_build(2, 5, 0, 10, p, p, p, p, p, p, p, p, p, None, None) == E
+    assert L.graft_treegraft_build(2, 5, 10, 10, p, p, None, p, p, p, p, p, p, None, None) == E
+    assert L.graft_treegraft_build(0, 5, 10, 10, None, None, None, None, None, None, None, None, None, None, None) == 0

@@ -8,6 +8,7 @@ from oracle import accept as OAcc
 from oracle import kv as OKV
 from oracle import sample as OS
 from oracle import tail as OTail
+from oracle import treegraft as OTG
 from oracle import attention as OA
 from oracle import lmhead as OL
 from oracle import table as OTab
@@ -667,6 +668,56 @@ def test_build_static_replace_matches_oracle(api):
     for key in ("n", "parent", "token", "depth", "pos", "mask", "src"):
         assert np.array_equal(got[key], exp[key]), key
     assert (got["src"] == 3).sum() > 100
+
+
+# ----------------------------------------------------------------------------- TreeGraft construction
+
+def test_treegraft_build_matches_oracle_and_feeds_the_prune(api):
+    """Six schedules of small and mid steps (D 5, W 10, m 10) against the
+    oracle, bit-exact (parents, tokens, fp32 scores); the result pruned to 63
+    by graft_build_tree equals the oracle's prune; a request whose candidate
+    slot has the wrong size is flagged and left unwritten."""
+    r = np.random.default_rng(63)
+    D, W, m, V = 5, 10, 10, 5000
+    masks = [0b00000, 0b00100, 0b01010, 0b11111, 0b00001, 0b10000, 0b00110]
+    B = len(masks)
+    counts = [api.graft_treegraft_node_count(D, W, m, mk) for mk in masks]
+    assert counts == [OTG.node_count(D, W, m, mk) for mk in masks]
+    sizes = counts[:-1] + [counts[-1] + 1]          # the last request's slot is one too big
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    tok = r.integers(0, V, (B, D, W, m)).astype(np.int32)
+    prob = np.sort(r.dirichlet(np.full(m, 0.3), (B, D, W)), axis=-1)[..., ::-1].astype(np.float32).copy()
+    q = r.random(int(off[-1])).astype(np.float32)
+    roots = r.integers(0, V, B).astype(np.int32)
+    tot = int(off[-1])
+    cp = torch.full((tot,), -7, dtype=torch.int32, device="cuda")
+    ct = torch.full((tot,), -7, dtype=torch.int32, device="cuda")
+    cs = torch.full((tot,), -7.0, dtype=torch.float32, device="cuda")
+    err = err_buf()
+    api.graft_treegraft_build(D, W, m, dev_i32(masks), dev_i32(roots), dev_i32(tok), torch.from_numpy(prob).cuda(),
+                              torch.from_numpy(q).cuda(), dev_i32(off), cp, ct, cs, err)
+    torch.cuda.synchronize()
+    assert err.item() == ERR_CAPACITY
+    gp, gt, gs = cp.cpu().numpy(), ct.cpu().numpy(), cs.cpu().numpy()
+    cands = []
+    for b in range(B - 1):
+        o0, o1 = int(off[b]), int(off[b + 1])
+        par, tk, sc = OTG.build(int(roots[b]), D, W, m, masks[b], tok[b], prob[b], q[o0:o1])
+        assert gp[o0:o1].tolist() == par, b
+        assert gt[o0:o1].tolist() == tk, b
+        assert np.array_equal(gs[o0:o1], np.array(sc, np.float32)), b
+        cands.append((gp[o0:o1], gt[o0:o1], gs[o0:o1]))
+    assert np.all(gp[off[-2]:] == -7)  # the flagged request was not written
+    got, row_off, err2 = _build_gpu(api, 0, cands, [63] * len(cands), None, [100] * len(cands), [63] * len(cands),
+                                    V=V)
+    assert err2 == 0
+    exp = OTree.build_batch(np.concatenate([c[0] for c in cands]), np.concatenate([c[1] for c in cands]),
+                            np.concatenate([c[2] for c in cands]),
+                            np.concatenate([[0], np.cumsum([len(c[0]) for c in cands])]), [63] * len(cands),
+                            np.zeros(0), np.zeros(0), np.zeros(len(cands) + 1, np.int32), [100] * len(cands), V,
+                            row_off)
+    for key in ("n", "parent", "token", "depth", "pos", "mask", "src"):
+        assert np.array_equal(got[key], exp[key]), key
 
 
 # ----------------------------------------------------------------------------- Graft-TAIL
