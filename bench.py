@@ -133,8 +133,7 @@ def main():
         return W.plant_hidden(wl, lambda ids: w[ids], tree["parent"], tree["token"], tree["n"],
                               ri.row_off)[0]
 
-    vr.step_update_retrieve()
-    vr.step_build_tree()
+    vr.build_only()
     torch.cuda.synchronize()
     tree0 = vr.tree_host()
     vr.set_hidden(plant(tree0))

@@ -64,7 +64,8 @@ class VerifyRound:
         else:
             base = STEPS_FUSED if fused else STEPS_SPLIT
         self.tail = bool(getattr(ri.wl, "tail", False))
-        self.steps = (("tail_cut",) if self.tail else ()) + base + (("kv_compact",) if chain else ())
+        pre = ("tail_cut",) if self.tail else (("treegraft",) if getattr(ri, "tg_tok", None) is not None else ())
+        self.steps = pre + base + (("kv_compact",) if chain else ())
         wl = ri.wl
         self.ri, self.wl, self.dev = ri, wl, dev
         B, N, k, V = ri.B, ri.N, ri.k, ri.V
@@ -84,11 +85,28 @@ class VerifyRound:
         self.tmpl_off = _i32(off, dev)
 
         self.table = _i32(ri.table, dev)
-        self.cand_parent = _i32(ri.cand_parent, dev)
-        self.cand_token = _i32(ri.cand_token, dev)
-        self.cand_score = torch.from_numpy(np.ascontiguousarray(ri.cand_score, np.float32)).to(dev)
-        self.cand_off = _i32(ri.cand_off, dev)
-        self.max_cand = int(np.max(np.diff(ri.cand_off)))
+        self.treegraft = getattr(ri, "tg_tok", None) is not None
+        if self.treegraft:
+            # TreeGraft: the candidates are built on the device every round
+            # (graft_treegraft_build) from the drafter stand-ins' outputs
+            counts = [api.graft_treegraft_node_count(wl.D, wl.Wf, wl.m, int(mk)) for mk in ri.tg_mask]
+            cand_off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+            self.tg_mask = _i32(ri.tg_mask, dev)
+            self.tg_tok = _i32(ri.tg_tok, dev)
+            self.tg_prob = torch.from_numpy(np.ascontiguousarray(ri.tg_prob, np.float32)).to(dev)
+            self.tg_q = torch.from_numpy(np.concatenate([ri.tg_q[b][:counts[b]] for b in range(B)])
+                                         .astype(np.float32)).to(dev)
+            self.cand_parent = torch.empty(int(cand_off[-1]), dtype=torch.int32, device=dev)
+            self.cand_token = torch.empty(int(cand_off[-1]), dtype=torch.int32, device=dev)
+            self.cand_score = torch.empty(int(cand_off[-1]), dtype=torch.float32, device=dev)
+        else:
+            cand_off = np.asarray(ri.cand_off, np.int32)
+            self.cand_parent = _i32(ri.cand_parent, dev)
+            self.cand_token = _i32(ri.cand_token, dev)
+            self.cand_score = torch.from_numpy(np.ascontiguousarray(ri.cand_score, np.float32)).to(dev)
+        self.cand_off_h = cand_off
+        self.cand_off = _i32(cand_off, dev)
+        self.max_cand = int(np.max(np.diff(cand_off)))
         self.budget = _i32(ri.budget, dev)
         self.ctx_len = _i32(ri.ctx_len, dev)
         # chained rounds plan attention for the largest context the cache
@@ -165,7 +183,7 @@ class VerifyRound:
             # workgroup); the pairs swap after each round
             self.ctx_alt = z(B)
             self.root_alt = z(B)
-            self.cand_root_idx = torch.from_numpy(np.asarray(ri.cand_off[:-1], np.int64)).to(dev)
+            self.cand_root_idx = torch.from_numpy(np.asarray(self.cand_off_h[:-1], np.int64)).to(dev)
 
     def set_hidden(self, hidden_bits):
         self.hidden = _bf16(hidden_bits.reshape(self.rows, self.wl.H), self.dev)
@@ -185,6 +203,12 @@ class VerifyRound:
                         rows=self.rows)
 
     # individual steps -------------------------------------------------
+    def step_treegraft(self):
+        wl = self.wl
+        api.graft_treegraft_build(wl.D, wl.Wf, wl.m, self.tg_mask, self.root_token, self.tg_tok, self.tg_prob,
+                                  self.tg_q, self.cand_off, self.cand_parent, self.cand_token, self.cand_score,
+                                  self.err)
+
     def step_tail_cut(self):
         api.graft_tail_cut(self.root_token, self.block_token, self.block_conf, self.wl.replace_thresh,
                            self.tail_keep, self.tail_root)
@@ -252,6 +276,14 @@ class VerifyRound:
     def step_accept(self):
         api.graft_accept(self.n_out, self.row_off, self.parent, self.token, self.topk_id, self.k,
                          self.acc_len, self.acc_path, self.bonus, self.err)
+
+    def build_only(self):
+        """Enqueue the round's steps up to and including the tree build (for a
+        first look at the tree, e.g. to plant the synthetic target on it)."""
+        for name in self.steps:
+            getattr(self, "step_" + name)()
+            if name == "build_tree":
+                return
 
     def run(self, events=None):
         """Enqueue one round.  `events`, if given, is a dict step -> list that

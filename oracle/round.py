@@ -23,6 +23,7 @@ from . import kv as _kv
 from . import lmhead as _lmhead
 from . import table as _table
 from . import tail as _tail
+from . import treegraft as _treegraft
 from . import template as _template
 from . import topk as _topk
 from . import tree as _tree
@@ -34,6 +35,9 @@ def tree_stage(ri, dmax: int = 8):
     table = _table.update(ri.table, ri.prev_n, ri.prev_row_off, ri.prev_token, ri.prev_topk)
     if getattr(ri.wl, "tail", False):
         return _tail_tree_stage(ri, table, dmax)
+    cand_parent, cand_token, cand_score, cand_off = ri.cand_parent, ri.cand_token, ri.cand_score, ri.cand_off
+    if getattr(ri, "tg_tok", None) is not None:
+        cand_parent, cand_token, cand_score, cand_off = treegraft_candidates(ri)
     tp_all, tr_all, rt_all, off = [], [], [], [0]
     for b in range(ri.B):
         tp, tr, _ = _template.template(int(ri.n_ret[b]), ri.k, dmax)
@@ -47,12 +51,29 @@ def tree_stage(ri, dmax: int = 8):
     ret_token = np.array(rt_all, np.int32)
     tmpl_off = np.array(off, np.int32)
     wl = ri.wl
-    tree = _tree.build_batch(ri.cand_parent, ri.cand_token, ri.cand_score, ri.cand_off,
+    tree = _tree.build_batch(cand_parent, cand_token, cand_score, cand_off,
                              ri.budget, ret_token, tparent, tmpl_off, ri.ctx_len, ri.V,
                              ri.row_off, static_replace=wl.static_replace, table=table,
                              replace_thresh=wl.replace_thresh)
     return dict(table=table, tparent=tparent, trank=trank, tmpl_off=tmpl_off,
                 ret_token=ret_token, tree=tree)
+
+
+def treegraft_candidates(ri):
+    """TreeGraft workloads: each request's candidates built by the shared-tree
+    construction (oracle.treegraft) from its drafter outputs and schedule,
+    with the current root token.  Returns (parent, token, score, cand_off)."""
+    wl = ri.wl
+    par, tok, sc, off = [], [], [], [0]
+    for b in range(ri.B):
+        n = _treegraft.node_count(wl.D, wl.Wf, wl.m, int(ri.tg_mask[b]))
+        p, t, s = _treegraft.build(int(ri.root_token[b]), wl.D, wl.Wf, wl.m, int(ri.tg_mask[b]), ri.tg_tok[b],
+                                   ri.tg_prob[b], ri.tg_q[b][:n])
+        par += p
+        tok += t
+        sc += s
+        off.append(off[-1] + n)
+    return (np.array(par, np.int32), np.array(tok, np.int32), np.array(sc, np.float32), np.array(off, np.int32))
 
 
 def _tail_tree_stage(ri, table, dmax: int):
@@ -121,10 +142,11 @@ def next_round_inputs(ri, ts, topk_id, acc_len, acc_path, bonus):
     nxt.kcache, nxt.vcache = kc[0], vc[0]
     nxt.ctx_len = ctx_next.astype(np.int32)
     nxt.root_token = root_next.astype(np.int32)
-    cand_token = np.array(ri.cand_token, np.int32).copy()
-    for b in range(B):
-        cand_token[int(ri.cand_off[b])] = int(bonus[b])
-    nxt.cand_token = cand_token
+    if ri.cand_token is not None:
+        cand_token = np.array(ri.cand_token, np.int32).copy()
+        for b in range(B):
+            cand_token[int(ri.cand_off[b])] = int(bonus[b])
+        nxt.cand_token = cand_token
     nxt.table = ts["table"]
     nxt.prev_n = np.array(tree["n"], np.int32)
     nxt.prev_row_off = np.array(ri.row_off, np.int32)

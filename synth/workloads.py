@@ -58,6 +58,7 @@ class Workload:
     Wf: int = 10      # drafter frontier width
     m: int = 10       # children per frontier node
     tail: bool = False  # Graft-TAIL on a block draft of n_nodes - 1 tokens
+    mid_mask: int = -1  # >= 0: TreeGraft shared tree built on the device (bit k: step k by the mid drafter)
 
     def with_ctx(self, lo: int, hi: int | None = None) -> "Workload":
         d = dict(self.__dict__)
@@ -96,6 +97,10 @@ WORKLOADS = {
                    "cut at confidence < 0.5, tails from a shared 151936x8 table",
                 B=4, Hq=32, Hkv=8, d=128, H=4096, V=151936, k=8, ctx_lo=4096, ctx_hi=4096,
                 tree="block", n_nodes=17, draft_budget=17, n_retrieved=16, tail=True, replace_thresh=0.5),
+    7: Workload(7, "TreeGraft shared tree: Qwen3-8B shapes, batch 1, ctx 32768, D=5 W=10 m=10 with the mid "
+                   "drafter at step 2, pruned to Bver=63, lm-head 4096x151936, table 151936x10",
+                B=1, Hq=32, Hkv=8, d=128, H=4096, V=151936, k=10, ctx_lo=32768, ctx_hi=32768,
+                tree="treegraft", n_nodes=63, draft_budget=63, n_retrieved=0, mid_mask=0b00100),
 }
 
 
@@ -158,6 +163,17 @@ def block_draft(r: np.random.Generator, V: int, L: int, root_token: int):
     parent = np.arange(-1, L, dtype=np.int32)
     score = np.concatenate([[1.0], conf]).astype(np.float32)
     return parent, tokens, score
+
+
+def treegraft_drafter_outputs(r: np.random.Generator, V: int, D: int, Wf: int, m: int, n_nodes: int):
+    """Stand-ins for TreeGraft's two drafters: for step k and frontier rank j,
+    m distinct child tokens with edge probabilities Dirichlet(0.3) sorted
+    descending (tok, prob [D][Wf][m]); and the mid drafter's probability of
+    the edge into every node, by creation index (q [n_nodes], U(0.05, 1))."""
+    tok = np.stack([np.stack([_distinct_tokens(r, V, m) for _ in range(Wf)]) for _ in range(D)]).astype(np.int32)
+    prob = np.sort(r.dirichlet(np.full(m, 0.3), (D, Wf)), axis=-1)[..., ::-1].astype(np.float32).copy()
+    q = r.uniform(0.05, 1.0, n_nodes).astype(np.float32)
+    return tok, prob, q
 
 
 def random_tree(r: np.random.Generator, V: int, N: int, root_token: int,
@@ -300,11 +316,16 @@ def make_round_inputs(wl: Workload, kv: bool = True, extra_slots: int = 0) -> Ro
         ctx_tok = context_tokens(rng(cfg, "context"), int(ctx_len[0]), V)
         table = warm_table_from_context(table, ctx_tok)
 
-    cp, ct, cs, coff, roots = [], [], [], [0], []
+    cp, ct, cs, coff, roots, tg_out = [], [], [], [0], [], []
     for b in range(B):
         rb = rng(cfg, f"draft/{b}")
         root = int(ctx_tok[-1]) if ctx_tok is not None else int(rb.integers(0, V))
-        if wl.tree == "random":
+        if wl.tree == "treegraft":
+            # drafter outputs only: the candidate tree is what the method builds
+            tg_out.append(treegraft_drafter_outputs(rb, V, wl.D, wl.Wf, wl.m, 1 + wl.D * wl.Wf * wl.m))
+            roots.append(root)
+            continue
+        elif wl.tree == "random":
             p, t, s = random_tree(rb, V, N, root)
         elif wl.tree == "block":
             p, t, s = block_draft(rb, V, N - 1, root)
@@ -328,8 +349,8 @@ def make_round_inputs(wl: Workload, kv: bool = True, extra_slots: int = 0) -> Ro
     ri = RoundInputs(
         wl=wl, B=B, N=N, k=k, V=V,
         ctx_len=ctx_len, ctx_tokens=ctx_tok,
-        cand_parent=np.concatenate(cp), cand_token=np.concatenate(ct),
-        cand_score=np.concatenate(cs), cand_off=np.array(coff, np.int32),
+        cand_parent=np.concatenate(cp) if cp else None, cand_token=np.concatenate(ct) if ct else None,
+        cand_score=np.concatenate(cs) if cs else None, cand_off=np.array(coff, np.int32) if cp else None,
         root_token=np.array(roots, np.int32),
         budget=np.full(B, wl.draft_budget, np.int32),
         n_ret=np.full(B, wl.n_retrieved, np.int32),
@@ -338,6 +359,11 @@ def make_round_inputs(wl: Workload, kv: bool = True, extra_slots: int = 0) -> Ro
         prev_n=prev_n, prev_row_off=prev_row_off, prev_token=prev_token, prev_topk=prev_topk,
         scale=float(1.0 / np.sqrt(wl.d)),
     )
+    if tg_out:  # TreeGraft: per request tok [D][W][m], prob [D][W][m], q [1 + D*W*m]
+        ri.tg_mask = np.full(B, wl.mid_mask, np.int32)
+        ri.tg_tok = np.stack([o[0] for o in tg_out])
+        ri.tg_prob = np.stack([o[1] for o in tg_out])
+        ri.tg_q = np.stack([o[2] for o in tg_out])
     if kv:
         make_qkv(ri, extra_slots)
     return ri

@@ -37,10 +37,10 @@ def _sample_nodes(rng, n, per_request):
     return nodes
 
 
-ATTN_SAMPLES = {1: 99, 2: 99, 3: 12, 4: 6, 5: 2, 6: 8}
+ATTN_SAMPLES = {1: 99, 2: 99, 3: 12, 4: 6, 5: 2, 6: 8, 7: 12}
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 7])
 def test_round_parity(cfg):
     _need_gpu()
     wl, ri, w, ts, hidden, vr = run_gpu_round(cfg)
@@ -193,7 +193,7 @@ def test_graph_replay_matches_eager(cfg, per_graph):
     say(f"[graph] cfg {cfg}: 4 replays of {per_graph} round(s) identical to eager rounds")
 
 
-@pytest.mark.parametrize("cfg,T", [(2, 0.0), (5, 0.0), (2, 1.0), (6, 0.0)])
+@pytest.mark.parametrize("cfg,T", [(2, 0.0), (5, 0.0), (2, 1.0), (6, 0.0), (7, 0.0)])
 def test_chained_rounds_match_oracle(cfg, T):
     """Three rounds chained on the GPU (KV compaction, context advance, bonus
     token as the next root) against the oracle's chain, round by round: the
@@ -265,11 +265,12 @@ def test_chained_rounds_match_oracle(cfg, T):
         assert np.array_equal(gv, nxt.vcache), f"round {rnd}: V cache after compaction"
         assert vr.ctx_len.cpu().numpy().tolist() == nxt.ctx_len.tolist()
         assert vr.root_token.cpu().numpy().tolist() == nxt.root_token.tolist()
-        assert np.array_equal(vr.cand_token.cpu().numpy(), nxt.cand_token)
+        if nxt.cand_token is not None:  # TreeGraft rebuilds its candidates from the root each round
+            assert np.array_equal(vr.cand_token.cpu().numpy(), nxt.cand_token)
         moved += sum(lens)
         state = nxt
-    if T == 0:
-        assert moved > 0  # the planted target accepts drafts, so rows did move
+    if T == 0 and cfg in (2, 5, 6):
+        assert moved > 0  # the planted target accepts drafts there, so rows did move
     say(f"[chain] cfg {cfg}: {R} chained rounds match the oracle; contexts {state.ctx_len.tolist()[:4]}")
 
 
