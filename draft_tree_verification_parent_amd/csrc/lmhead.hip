@@ -11,17 +11,19 @@
 //
 // Two weight layouts:
 //  * packed (graft_lmhead_pack, done once when the weights are loaded): W
-//    is cut into stage images of 128 vocabulary rows x 128 hidden columns
-//    (32 KB), stored tile by tile, chunk by chunk, so a workgroup's whole
-//    weight stream is one contiguous, linearly read region.  Inside an image
-//    row r keeps its 16-byte pieces in XOR-swizzled order (piece p at slot
-//    p ^ (r & 15)), so 16 lanes reading one MFMA fragment column hit all
-//    LDS banks once.  A persistent grid (one 144 KB workgroup per CU) copies
-//    images HBM -> LDS with global_load_lds_dwordx4 (LDS DMA: no registers,
-//    in a 3-stage ring that runs across tile boundaries), stages the hidden
-//    chunk the same way, and reads both MFMA operands from LDS.
-//    Linear reads reach about 7.2 TB/s on MI355X where row-major tiles
-//    (256-byte runs per row) stall near 5.6 TB/s.
+//    is cut into images of 128 vocabulary rows x 64 hidden columns (16 KB,
+//    row-major inside), stored tile by tile, column chunk by column chunk,
+//    so a workgroup's whole weight stream is one contiguous, linearly read
+//    region whatever its stage width.  A persistent grid (one workgroup per
+//    CU) copies images HBM -> LDS with global_load_lds_dwordx4 (LDS DMA: no
+//    registers, in a ring that runs across tile boundaries), stages the
+//    hidden chunk the same way, and reads both MFMA operands from LDS.  The
+//    DMA lands 16 bytes per lane at consecutive LDS addresses, and the
+//    per-lane source offsets pick which piece lands where: LDS rows are
+//    XOR-swizzled so 16 lanes reading one MFMA fragment column hit 16
+//    different bank groups.  Linear reads reach about 7.2 TB/s on MI355X
+//    where row-major tiles (256-byte runs per row) stall near 5.6 TB/s, and
+//    128-byte runs at a 256-byte stride near 3.2 TB/s.
 //  * row-major W [V, H]: W read straight from HBM into MFMA operand
 //    registers (ping-pong buffers), the hidden chunk double-buffered in LDS.
 // Fused top-k: each logit tile goes through LDS and 4 threads per row rank
@@ -32,6 +34,7 @@
 // workgroup's tiles, so the merge reads one list per (row, workgroup).
 #include <climits>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -49,6 +52,16 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBV = kWaves * 32;
 
 __device__ inline bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// f(integral_constant<int, i>) for i = 0 .. N - 1, unrolled at compile time
+template <typename F, int... I>
+__device__ inline void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 __device__ inline u32x4 zero4() { return u32x4{0u, 0u, 0u, 0u}; }
 
 template <int KC, bool FUSED, int K>
@@ -223,7 +236,8 @@ __global__ __launch_bounds__(kThreads, 4) void lmhead_kernel(int M, int H, int V
 constexpr int PK_BV = 128;                  // vocabulary rows per tile
 constexpr int PK_KC = 128;                  // hidden columns per chunk
 constexpr int PK_NS = 3;                    // LDS ring stages
-constexpr int PK_WB = PK_BV * PK_KC * 2;    // 32 KB stage image of W
+constexpr int PK_WB = PK_BV * PK_KC * 2;    // 32 KB of W per stage (two packed images)
+constexpr int PK_IMG = PK_BV * 64 * 2;      // 16 KB packed image: 128 rows x 64 columns
 constexpr int PK_HB = BM * PK_KC * 2;       // 16 KB hidden chunk
 constexpr int PK_SB = PK_WB + PK_HB;        // one ring stage
 constexpr int PK_GRID = 256;                // persistent workgroups (one per MI355X CU)
@@ -234,20 +248,20 @@ constexpr int PK_WAVES = GRAFT_PK_WAVES;    // wavefronts per packed-path workgr
 constexpr int PK_TSTR = PK_BV + 4;          // floats per row of the staged logit tile
 static_assert(BM * PK_TSTR * 4 <= PK_SB, "logit tile must fit in one ring stage");
 
-// Image (tile t, chunk c) at byte ((t * nch + c) * PK_WB); inside it, byte
-// r * 256 + p * 16 holds W[128 t + r][128 c + 8 (p ^ (r & 15)) .. + 8], zero
-// for rows >= V.  One thread per 16-byte piece.
+// Image (tile t, column chunk j) at byte ((t * (H / 64) + j) * PK_IMG);
+// inside it, byte r * 128 + p * 16 holds W[128 t + r][64 j + 8 p .. + 8],
+// zero for rows >= V.  One thread per 16-byte piece.
 __global__ __launch_bounds__(256) void lmhead_pack_kernel(int H, int V, const graft_bf16 *__restrict__ w,
                                                           u32x4 *__restrict__ out, size_t pieces) {
   const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= pieces) return;
-  const int nch = H / PK_KC;
-  const int p = static_cast<int>(i & 15);
-  const int r = static_cast<int>((i >> 4) & (PK_BV - 1));
-  const size_t img = i >> 11;  // 2048 pieces per image
-  const int c = static_cast<int>(img % nch);
-  const size_t row = (img / nch) * PK_BV + r;
-  const int col = c * PK_KC + 8 * (p ^ (r & 15));
+  const int nkc = H / 64;
+  const int p = static_cast<int>(i & 7);
+  const int r = static_cast<int>((i >> 3) & (PK_BV - 1));
+  const size_t img = i >> 10;  // 1024 pieces per image
+  const int j = static_cast<int>(img % nkc);
+  const size_t row = (img / nkc) * PK_BV + r;
+  const int col = j * 64 + 8 * p;
   out[i] = row < static_cast<size_t>(V) ? *reinterpret_cast<const u32x4 *>(w + row * H + col) : zero4();
 }
 
@@ -341,11 +355,20 @@ __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H,
   // LDS byte address of the ring (the M0 base of the DMAs)
   const unsigned sbase = static_cast<unsigned>(reinterpret_cast<size_t>((__attribute__((address_space(3))) void *)sm));
 
+  // W images stream through L2 non-temporally unless several m tiles
+  // (workgroups of one XCD) read each image
+  const bool w_nt = tiles_m == 1;
   // loop-invariant DMA source offsets: W images are copied linearly; hidden
   // row r (clamped to M - 1) lands swizzled like the images
   unsigned wo[WI], ho[HI];
 #pragma unroll
-  for (int i = 0; i < WI; ++i) wo[i] = ((wave * WI + i) * 64 + lane) * 16;
+  for (int i = 0; i < WI; ++i) {
+    // LDS row r holds logical piece p at slot p ^ (r & 15); pieces 0-7 come
+    // from the chunk's first packed image, 8-15 from the second
+    const int r = 4 * (wave * WI + i) + (lane >> 4);
+    const int p = (lane & 15) ^ (r & 15);
+    wo[i] = static_cast<unsigned>((p >> 3) * PK_IMG + r * 128 + (p & 7) * 16);
+  }
 #pragma unroll
   for (int i = 0; i < HI; ++i) {
     const int r = 4 * (wave * HI + i) + (lane >> 4);
@@ -363,7 +386,10 @@ __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H,
 #pragma unroll
     for (int i = 0; i < HI; ++i) lds_dma16_cached(hl + i * 1024, hsrc, ho[i]);
 #pragma unroll
-    for (int i = 0; i < WI; ++i) lds_dma16(wl + i * 1024, wsrc, wo[i]);
+    for (int i = 0; i < WI; ++i) {
+      if (w_nt) lds_dma16(wl + i * 1024, wsrc, wo[i]);
+      else lds_dma16_cached(wl + i * 1024, wsrc, wo[i]);
+    }
   };
 
   f32x4 acc[VBW][4];
@@ -552,6 +578,317 @@ __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H,
   }
 }
 
+// ------------------------------------------------------ packed W, wide tiles
+// Past 128 hidden rows the product leaves the HBM bound: at M = 960 it needs
+// 0.49 ms of bf16 MFMA at the dense peak against 0.16 ms to stream W.  The
+// 64-row kernel above would re-read every W image once per 64 rows, and its
+// 16 x 64 wave tiles spend more LDS bandwidth than MFMA time.  Here a
+// workgroup of 4 wavefronts computes a tile of 128 hidden rows x BV
+// vocabulary rows, each wavefront a 64 x (BV / 2) block (2 x 2 layout), so
+// one 16-byte fragment read feeds 8 / 3 MFMAs (BV = 256) and every byte a
+// CU takes in feeds 85 flops.  That ratio is what bounds the kernel on
+// MI355X: once HBM misses share a CU's request stream (and its in-order
+// completion) the CU takes in about 30-35 GB/s, hits and misses alike.
+//
+// The ring stages 64 hidden columns at a time, one packed image per 128
+// vocabulary rows (3 x 48 KB for BV = 256).  In LDS a row takes 128 bytes:
+// row r sits at line r ^ ((r >> 3) & 1) with its 16-byte pieces
+// XOR-swizzled by (r % 8), so any 8 lanes of a fragment read (rows r0 ..
+// r0 + 7) hit 8 different 16-byte bank groups of a 128-byte span, and any
+// 16 (rows r0 .. r0 + 15) 16 different ones of a 256-byte span.  Each DMA
+// instruction fills eight lines from eight consecutive rows of one image
+// (1 KB of contiguous source), so the image index is a scalar; the last
+// tile's second image is clamped to the last image (its rows are all past
+// V).
+//
+// Epilogue (per tile): the stage of the tile's last chunk is free until the
+// next ring barrier; the 128 x BV logits go through it in 4 passes of 32
+// rows.  8 threads per row screen BV / 8 entries each (interleaved 16-byte
+// units, so the reads are conflict-free) into 4 persistent sorted lists per
+// thread, one per pass; the bounds are those of the 64-row kernel.  One
+// list per (row, workgroup) is written at the end, merged by
+// topk_merge_kernel.  The k-order of the MFMA sums is that of every other
+// path, so the logits are bit-identical.
+constexpr int WD_BM = 128;  // hidden rows per tile
+constexpr int WD_KC = 64;   // hidden columns per ring stage
+
+__device__ inline const unsigned char *wd_uniform(const unsigned char *p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const unsigned char *>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// LDS byte offset of logical piece P (8 bf16) of row r in a stage region
+__device__ inline int wd_piece(int r, int P) { return ((r ^ ((r >> 3) & 1)) << 7) + ((P ^ (r & 7)) << 4); }
+
+// Wait until at most n * D of this wave's DMAs are outstanding (n <= NMAX,
+// picked at run time; vmcnt takes an immediate), then meet the other waves.
+template <int D, int J, int NMAX>
+__device__ inline void ring_barrier_n(int n) {
+  static_assert(D * NMAX < 64, "vmcnt holds 6 bits");
+  if constexpr (J >= NMAX) {
+    ring_barrier<J * D>();
+  } else {
+    if (n == J) ring_barrier<J * D>();
+    else ring_barrier_n<D, J + 1, NMAX>(n);
+  }
+}
+
+template <int BV, int NS, int K>
+__global__ __launch_bounds__(256, 1) void lmhead_wide_kernel(int M, int H, int V, int k,
+                                                           const graft_bf16 *__restrict__ hidden,
+                                                           const unsigned char *__restrict__ wpk,
+                                                           uint64_t *__restrict__ part_out, int tiles_m,
+                                                           int tiles_v, int n_img) {
+  static_assert(BV == 128 || BV == 256, "one or two packed images per tile");
+  constexpr int WB = BV * WD_KC * 2;     // W bytes per stage
+  constexpr int HB = WD_BM * WD_KC * 2;  // hidden bytes per stage
+  constexpr int SB = WB + HB;
+  constexpr int WI = WB / 4096;          // W DMAs per wave per stage (1 KB each)
+  constexpr int HI = HB / 4096;          // hidden DMAs per wave per stage
+  constexpr int VW = BV / 2;             // vocabulary rows per wave
+  constexpr int VB = VW / 16;            // 16-row MFMA blocks per wave
+  constexpr int TSTR = BV + 4;           // floats per staged logit row
+  constexpr int UPT = BV / 32;           // 16-byte units per screening thread
+  constexpr int EPT = UPT * 4;           // entries per screening thread
+  constexpr int GPT = EPT / 8;           // groups of 8 entries per thread
+  static_assert(32 * TSTR * 4 <= SB, "32 staged logit rows must fit in one stage");
+  static_assert(NS >= 3 && NS * SB <= 160 * 1024, "ring of 3+ stages in 160 KB of LDS");
+  __shared__ __attribute__((aligned(1024))) unsigned char sm[NS * SB];
+
+  const PkMap map = pk_map(blockIdx.x, tiles_m);
+  if (map.stream < 0) return;
+  const int S = map.streams;
+  const int m0 = map.tm * WD_BM;
+  const int nkc = H / WD_KC;
+  const int items = map.stream < tiles_v ? (tiles_v - map.stream + S - 1) / S : 0;
+  const int Q = items * nkc;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wv = wave & 1;
+  const unsigned sbase = static_cast<unsigned>(reinterpret_cast<size_t>((__attribute__((address_space(3))) void *)sm));
+
+  // DMA source offsets: lane -> (line, slot) -> (row, logical piece) ->
+  // its place in the row-major packed image (W) or the row-major hidden
+  // state (rows clamped to M - 1).  The line -> row map is its own inverse.
+  unsigned wo[WI], ho[HI];
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int L = 8 * (wave * WI + i) + (lane >> 3);
+    const int r = L ^ ((L >> 3) & 1);
+    const int P = (lane & 7) ^ (r & 7);
+    wo[i] = static_cast<unsigned>((r & (PK_BV - 1)) * 128 + (P << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < HI; ++i) {
+    const int L = 8 * (wave * HI + i) + (lane >> 3);
+    const int r = L ^ ((L >> 3) & 1);
+    const int P = (lane & 7) ^ (r & 7);
+    const int m = min(m0 + r, M - 1);
+    ho[i] = static_cast<unsigned>(m) * H * 2 + (P << 4);
+  }
+  // DMA issue, one instruction at a time: d < HI hidden, else W.  prep(q)
+  // sets the scalar bases of stage q.
+  const unsigned char *dw = wpk, *dh = reinterpret_cast<const unsigned char *>(hidden);
+  unsigned dwl = sbase, dhl = sbase;
+  auto prep = [&](int q) {
+    const int st = q % NS;
+    const int item = q / nkc;
+    const int kc = q - item * nkc;
+    const int tv = map.stream + item * S;
+    const int img = min(tv * (BV / PK_BV) + (BV == 256 ? (wave >> 1) : 0), n_img - 1);
+    dw = wd_uniform(wpk + (static_cast<size_t>(img) * nkc + kc) * PK_IMG);
+    dh = wd_uniform(reinterpret_cast<const unsigned char *>(hidden) + kc * WD_KC * 2);
+    dwl = sbase + st * SB + wave * WI * 1024;
+    dhl = sbase + st * SB + WB + wave * HI * 1024;
+  };
+  auto dma = [&](auto d_tag) {
+    constexpr int d = decltype(d_tag)::value;
+    if constexpr (d < HI) lds_dma16_cached(dhl + d * 1024, dh, ho[d]);
+    else lds_dma16_cached(dwl + (d - HI) * 1024, dw, wo[d - HI]);
+  };
+
+  // fragment offsets inside a stage (k-step s adds 4 to the logical piece)
+  int fa[VB][2], fb[4][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) fa[vb][s] = wd_piece(wv * VW + vb * 16 + l16, s * 4 + g);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) fb[mb][s] = WB + wd_piece(wm * 64 + mb * 16 + l16, s * 4 + g);
+  }
+  // 16-row blocks of this wave holding rows < M (wave-uniform)
+  const int nmb = max(0, min(4, (M - m0 - wm * 64 + 15) >> 4));
+
+  f32x4 acc[VB][4];
+#pragma unroll
+  for (int a = 0; a < VB; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  graft::TopKeys<K> lists[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) lists[p].init();
+
+  const int srow = tid >> 3;  // screening: row srow of each 32-row pass
+  const int part = tid & 7;
+
+  constexpr int ND = WI + HI;  // DMAs per wave per stage
+  // Software pipeline: the fragments of the next k-step are read while the
+  // MFMAs of the current one run, and the next stage's DMAs are spread over
+  // the first k-step's MFMA groups, so neither the LDS reads nor the
+  // memory pipeline's back-pressure stall the MFMAs.  The ring barrier
+  // sits between the two k-steps: it waits for stage q + 1 (and, for every
+  // wave, the end of the reads of stage q), after which the first
+  // fragments of stage q + 1 are read under the second k-step's MFMAs.
+  auto load_frags = [&](const unsigned char *st, int s, bf16x8 (&a)[VB], bf16x8 (&b)[4]) {
+#pragma unroll
+    for (int vb = 0; vb < VB; ++vb) a[vb] = *reinterpret_cast<const bf16x8 *>(st + fa[vb][s]);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) b[mb] = *reinterpret_cast<const bf16x8 *>(st + fb[mb][s]);
+  };
+  auto mfma_vb = [&](int vb, const bf16x8 (&a)[VB], const bf16x8 (&b)[4]) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      acc[vb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[vb], b[mb], acc[vb][mb], 0, 0, 0);
+  };
+  // k-step 0 of a stage, with (ISS) the DMAs of the stage prep() chose
+  auto kstep0 = [&](auto iss_tag, const bf16x8 (&a)[VB], const bf16x8 (&b)[4]) {
+    constexpr bool ISS = decltype(iss_tag)::value;
+    static_for<VB>([&](auto vb_tag) {
+      constexpr int vb = decltype(vb_tag)::value;
+      if constexpr (ISS) {
+        static_for<(vb + 1) * ND / VB - vb * ND / VB>([&](auto j_tag) {
+          dma(std::integral_constant<int, vb * ND / VB + decltype(j_tag)::value>{});
+        });
+      }
+      mfma_vb(vb, a, b);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // a wave whose 64 rows all lie past M skips its MFMAs (uniform)
+  const bool live = nmb > 0;
+
+  bf16x8 a0[VB], b0[4], a1[VB], b1[4];
+  for (int q = 0; q < NS - 1 && q < Q; ++q) {
+    prep(q);
+    static_for<ND>([&](auto d_tag) { dma(d_tag); });
+  }
+  if (Q > 0) {
+    ring_barrier_n<ND, 0, NS - 2>(min(NS - 2, Q - 1));
+    load_frags(sm, 0, a0, b0);
+  }
+  for (int q = 0; q < Q; ++q) {
+    const unsigned char *st = sm + (q % NS) * SB;
+    load_frags(st, 1, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool iss = q + NS - 1 < Q;
+    if (iss) prep(q + NS - 1);  // into the stage chunk q - 1 used
+    if (live) {
+      if (iss) kstep0(std::true_type{}, a0, b0);
+      else kstep0(std::false_type{}, a0, b0);
+    } else if (iss) {
+      static_for<ND>([&](auto d_tag) { dma(d_tag); });
+    }
+    if (q + 1 < Q) {
+      // stage q + 1 has landed once only the stages issued after it may be in flight
+      ring_barrier_n<ND, 0, NS - 2>(min(NS - 2, Q - 2 - q));
+      load_frags(sm + ((q + 1) % NS) * SB, 0, a0, b0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (live) {
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) mfma_vb(vb, a1, b1);
+    }
+    const int item = q / nkc;
+    if (q - item * nkc != nkc - 1) continue;
+
+    // ---- tile done
+    const int v0 = (map.stream + item * S) * BV;
+    float *s_t = reinterpret_cast<float *>(sm + (q % NS) * SB);
+    __syncthreads();  // every wave is done reading the stage
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      if (wm == (p >> 1)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int mb = 2 * (p & 1) + h;
+#pragma unroll
+          for (int vb = 0; vb < VB; ++vb)
+            *reinterpret_cast<f32x4 *>(&s_t[(h * 16 + l16) * TSTR + wv * VW + vb * 16 + 4 * g]) = acc[vb][mb];
+        }
+      }
+      __syncthreads();
+      // unit u of this thread: 16-byte column 2 * part + (u & 1) + 16 * (u >> 1)
+      const float *src = &s_t[srow * TSTR];
+      float xv[EPT];
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int c = 4 * (2 * part + (u & 1) + 16 * (u >> 1));
+        const float4 x = *reinterpret_cast<const float4 *>(src + c);
+        xv[4 * u] = v0 + c < V ? x.x : -INFINITY;
+        xv[4 * u + 1] = v0 + c + 1 < V ? x.y : -INFINITY;
+        xv[4 * u + 2] = v0 + c + 2 < V ? x.z : -INFINITY;
+        xv[4 * u + 3] = v0 + c + 3 < V ? x.w : -INFINITY;
+      }
+      // bound: the largest k-th key of the row's 8 lists; on the first tile
+      // also the k-th largest of the row's group maxima (groups of 8 entries)
+      const uint64_t thr = graft::group_max<8>(lists[p].k[K - 1]);
+      float bound = thr != 0 ? graft::key_value(thr) : -INFINITY;
+      if (item == 0) {
+        float gm[GPT];
+#pragma unroll
+        for (int q8 = 0; q8 < GPT; ++q8) {
+          float m8 = xv[8 * q8];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) m8 = fmaxf(m8, xv[8 * q8 + e]);
+          gm[q8] = m8;
+        }
+        float gk = -INFINITY;
+        for (int r = 0; r < k; ++r) {
+          float lm = gm[0];
+#pragma unroll
+          for (int q8 = 1; q8 < GPT; ++q8) lm = fmaxf(lm, gm[q8]);
+          const float best = graft::group_maxf<8>(lm);
+#pragma unroll
+          for (int q8 = 0; q8 < GPT; ++q8) gm[q8] = gm[q8] == best ? -INFINITY : gm[q8];
+          gk = best;
+        }
+        bound = fmaxf(bound, gk);
+      }
+      uint32_t pass = 0;
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) pass |= static_cast<uint32_t>(!(xv[j] < bound)) << j;
+      if (m0 + 32 * p + srow >= M) pass = 0;
+      while (pass != 0) {
+        const int j = __builtin_ctz(pass);
+        pass &= pass - 1;
+        const int c = 4 * (2 * part + ((j >> 2) & 1) + 16 * (j >> 3)) + (j & 3);
+        if (v0 + c < V) lists[p].insert(graft::rank_key(src[c], v0 + c));
+      }
+      __syncthreads();  // the next pass overwrites the staged rows
+    }
+#pragma unroll
+    for (int a = 0; a < VB; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // k best keys of each row over this workgroup's tiles (0 = no entry)
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int m = m0 + 32 * p + srow;
+    for (int j = 0; j < k; ++j) {
+      const uint64_t best = graft::group_max<8>(lists[p].k[0]);
+      if (lists[p].k[0] == best) lists[p].pop_front();
+      if (part == 0 && m < M) part_out[(static_cast<size_t>(m) * S + map.stream) * k + j] = best;
+    }
+  }
+}
+
 }  // namespace
 
 namespace graft {
@@ -563,9 +900,14 @@ size_t lmhead_fused_ws_bytes(int M, int V, int k) {
 
 namespace {
 int packed_tiles_m(int M) { return (M + BM - 1) / BM; }
+int wide_tiles_m(int M) { return (M + WD_BM - 1) / WD_BM; }
+// The fused packed path takes the wide tiles above 128 rows.  Up to 128
+// rows the product is bound by streaming W, and the 64-row kernel (its m
+// tiles sharing each image through L2) streams it faster.
+bool packed_wide(int M) { return M > 2 * BM; }
 size_t packed_fused_ws_bytes(int M, int k) {
-  const int T = packed_tiles_m(M);
-  if (T > PK_GRID) return 0;
+  const int T = packed_wide(M) ? wide_tiles_m(M) : packed_tiles_m(M);
+  if (packed_tiles_m(M) > PK_GRID) return 0;
   return static_cast<size_t>(M) * pk_map(0, T).streams * k * sizeof(uint64_t);
 }
 }  // namespace
@@ -643,6 +985,26 @@ extern "C" int graft_lmhead_topk(int M, int H, int V, int k, const graft_bf16 *h
       hipLaunchKernelGGL((lmhead_packed_kernel<F, Kv, PK_WAVES, false>), dim3(PK_GRID), dim3(PK_WAVES * 64), 0, s, M, H, V,
                          F ? k : 0, hidden, wpk, F ? nullptr : logits, pk, tiles_m, tiles_v, 1.0f, nullptr, nullptr);
     };
+    if (fused && packed_wide(M)) {
+      uint64_t *pk = static_cast<uint64_t *>(ws);
+      const int Tw = wide_tiles_m(M);
+      const int n_img = (V + PK_BV - 1) / PK_BV;
+      auto launch_w = [&](auto bv_tag, auto k_tag) {
+        constexpr int BVv = decltype(bv_tag)::value;
+        constexpr int Kv = decltype(k_tag)::value;
+        constexpr int NSv = BVv == 256 ? 3 : 4;
+        const int tv = (V + BVv - 1) / BVv;
+        hipLaunchKernelGGL((lmhead_wide_kernel<BVv, NSv, Kv>), dim3(PK_GRID), dim3(256), 0, s, M, H, V, k, hidden, wpk,
+                           pk, Tw, tv, n_img);
+      };
+      using I256 = std::integral_constant<int, 256>;
+      // (two images with 16-key lists would spill registers)
+      if (k <= 8) launch_w(I256{}, I8{});
+      else launch_w(I128{}, I16{});
+      int rc = graft::check_launch("lmhead (packed, wide tiles, fused top-k)");
+      if (rc != GRAFT_OK) return rc;
+      return graft::launch_topk_merge(M, pk_map(0, Tw).streams, k, pk, topk_id, topk_val, s);
+    }
     if (fused) {
       uint64_t *pk = static_cast<uint64_t *>(ws);
       if (k <= 8) launch(T{}, I8{}, pk);

@@ -296,10 +296,9 @@ int graft_lmhead_topk(int M, int H, int V, int k,
  * Weight packing for graft_lmhead_topk (done once, when the lm-head is
  * loaded; not part of a round).  w (device bf16 [V, H] row-major) is
  * rewritten into w_packed (device, graft_lmhead_pack_bytes(V, H) bytes,
- * caller-owned): images of 128 vocabulary rows x 128 hidden columns in
- * tile-major, chunk-minor order, each row's 16-byte pieces XOR-swizzled
- * by (row % 16), rows past V zero.  H % 128 == 0; returns 0 bytes /
- * GRAFT_EINVAL otherwise.
+ * caller-owned): images of 128 vocabulary rows x 64 hidden columns
+ * (row-major inside, 16 KB) in tile-major, column-chunk-minor order, rows
+ * past V zero.  H % 128 == 0; returns 0 bytes / GRAFT_EINVAL otherwise.
  */
 size_t graft_lmhead_pack_bytes(int V, int H);
 int graft_lmhead_pack(int V, int H, const graft_bf16 *w, graft_bf16 *w_packed, graft_stream stream);

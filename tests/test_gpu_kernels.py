@@ -138,15 +138,12 @@ def test_fused_lmhead_topk_equals_split(api, M, H, V, k):
 
 def _pack_np(w, V, H):
     """The packed layout as include/graft.h states it: images of 128 rows x
-    128 columns, tile-major then chunk; slot s of row r holds 16-byte piece
-    s ^ (r % 16); rows past V are zero."""
-    T, nch = (V + 127) // 128, H // 128
+    64 columns, row-major inside, tile-major then column chunk; rows past V
+    are zero."""
+    T, nkc = (V + 127) // 128, H // 64
     wp = np.zeros((T * 128, H), np.uint16)
     wp[:V] = w
-    x = wp.reshape(T, 128, nch, 16, 8).transpose(0, 2, 1, 3, 4)  # [T][c][r][piece][8]
-    r = np.arange(128)[:, None]
-    src = np.arange(16)[None, :] ^ (r % 16)
-    return x[:, :, r, src, :].reshape(-1)
+    return wp.reshape(T, 128, nkc, 64).transpose(0, 2, 1, 3).reshape(-1)
 
 
 def _packed(api, w, V, H):
@@ -190,10 +187,14 @@ def test_lmhead_packed_equals_rowmajor(api, M, H, V):
 
 
 @pytest.mark.parametrize("M,H,V,k", [(60, 4096, 128256, 8), (130, 384, 1001, 16), (1, 128, 5, 3),
-                                     (64, 256, 129, 10), (300, 128, 2000, 16), (2112, 128, 300, 8)])
+                                     (64, 256, 129, 10), (300, 128, 2000, 16), (2112, 128, 300, 8),
+                                     (68, 1024, 5000, 8), (65, 256, 130, 16), (960, 512, 4001, 8)])
 def test_fused_packed_topk_equals_split(api, M, H, V, k):
     """Packed fused top-k (lists kept per workgroup across tiles) ranks
-    exactly the logits the split row-major mode writes."""
+    exactly the logits the split row-major mode writes.  Up to 64 rows one
+    64-row tile per workgroup; above, 128-row tiles of one image (one m
+    tile) or two images (several m tiles, the last image clamped when the
+    image count is odd)."""
     say(f"[fused packed lmhead+topk] M={M} H={H} V={V} k={k}")
     r = np.random.default_rng(M * 11 + V)
     h = f32_to_bf16_bits(r.standard_normal((M, H)).astype(np.float32))
