@@ -31,6 +31,7 @@
 // and a merge kernel combines splits with the usual log-sum-exp weights.
 // With a single split the workgroup normalises and writes bf16 directly.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 
@@ -228,7 +229,9 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
   bool active[RBW];
 #pragma unroll
   for (int j = 0; j < RBW; ++j) {
-    const int rb0 = row_lo + (wave * RBW + j) * 16;
+    // row blocks are dealt round-robin (block j * 8 + wave), so the two waves
+    // of each SIMD carry at most one block more than any other pair
+    const int rb0 = row_lo + (j * kWaves + wave) * 16;
     // wave-uniform; readfirstlane lets the compiler branch on a scalar
     // instead of masking every MFMA below
     active[j] = __builtin_amdgcn_readfirstlane(rb0 < rows_total ? 1 : 0) != 0;
@@ -261,15 +264,19 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
   const int vfrag = vr * TL::ROW + 8 * ((vcol >> 2) & 1);
 
   // One chunk: S^T for its 64 keys, one online-softmax update per row
-  // block, then O^T += V^T . P^T over its two 32-key halves.
-  auto compute = [&](int c) {
+  // block, then O^T += V^T . P^T over its two 32-key halves.  NA, the
+  // number of active row blocks (always the first NA), is a compile-time
+  // constant so the MFMAs carry no branches and the fragment reads can be
+  // issued ahead of them.
+  auto compute = [&](auto na_tag, int c) {
+    constexpr int NA = decltype(na_tag)::value;
     const lds_u8 *ks = (const lds_u8 *)sm + (c % NS) * TL::SB;
     const lds_u8 *vs = ks + TL::KB;
     const int c0 = k_begin + c * KCH;
     // S^T blocks: sacc[j][kb][i] = S[row l16][key c0 + kb*16 + 4g + i]
     f32x4 sacc[RBW][4];
 #pragma unroll
-    for (int j = 0; j < RBW; ++j)
+    for (int j = 0; j < NA; ++j)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) sacc[j][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -279,8 +286,8 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
         const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8 *)(
             ks + 16 * kb * TL::ROW + kfrag + (((4 * s + g) ^ swk) * 16));
 #pragma unroll
-        for (int j = 0; j < RBW; ++j)
-          if (active[j]) sacc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j][s], sacc[j][kb], 0, 0, 0);
+        for (int j = 0; j < NA; ++j)
+          sacc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j][s], sacc[j][kb], 0, 0, 0);
       }
     }
     // online softmax (base 2).  A chunk that lies entirely inside the
@@ -288,8 +295,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
     const bool unmasked = c0 + KCH <= ctx && c0 + KCH <= k_end;
     bf16x8 pb[RBW][2];  // P^T operand of each 32-key half
 #pragma unroll
-    for (int j = 0; j < RBW; ++j) {
-      if (!active[j]) continue;
+    for (int j = 0; j < NA; ++j) {
       // raw scores; the scale is folded into the exp2 argument below
       float x[16];
       if (unmasked) {
@@ -358,22 +364,33 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
         const u32x2 hw = __builtin_bit_cast(u32x2, hi);
         const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], hw[0], hw[1]});
 #pragma unroll
-        for (int j = 0; j < RBW; ++j)
-          if (active[j]) oacc[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[j][t], oacc[j][db], 0, 0, 0);
+        for (int j = 0; j < NA; ++j)
+          oacc[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[j][t], oacc[j][db], 0, 0, 0);
       }
     }
   };
 
-  // ---- ring: chunks c+1 .. c+NS-2 stay in flight while chunk c is computed
+  // ---- ring: chunks c+1 .. c+NS-2 stay in flight while chunk c is computed.
+  // A wave without active row blocks still issues its share of every
+  // chunk's DMAs and meets the others at each barrier.
   constexpr int PER = 2 * DI;  // DMAs per wave per chunk
-  for (int c = 0; c < nch; ++c) {
-    const int younger = min(nch - 1 - c, NS - 2);  // chunks issued after c
-    if (younger >= 2) ring_barrier<2 * PER>();
-    else if (younger == 1) ring_barrier<PER>();
-    else ring_barrier<0>();
-    if (c + NS - 1 < nch) issue(c + NS - 1);  // into the stage chunk c - 1 used
-    compute(c);
-  }
+  auto run = [&](auto na_tag) {
+    for (int c = 0; c < nch; ++c) {
+      const int younger = min(nch - 1 - c, NS - 2);  // chunks issued after c
+      if (younger >= 2) ring_barrier<2 * PER>();
+      else if (younger == 1) ring_barrier<PER>();
+      else ring_barrier<0>();
+      if (c + NS - 1 < nch) issue(c + NS - 1);  // into the stage chunk c - 1 used
+      if constexpr (decltype(na_tag)::value > 0) compute(na_tag, c);
+    }
+  };
+  int nact = 0;  // active row blocks are the first nact (wave-uniform)
+#pragma unroll
+  for (int j = 0; j < RBW; ++j) nact += active[j] ? 1 : 0;
+  if (nact == 0) run(std::integral_constant<int, 0>{});
+  else if (RBW == 1 || nact == 1) run(std::integral_constant<int, 1>{});
+  else if (RBW == 2 || nact == 2) run(std::integral_constant<int, (RBW >= 2 ? 2 : 1)>{});
+  else run(std::integral_constant<int, (RBW >= 3 ? 3 : 1)>{});
 
   // ---- epilogue: oacc[j][db][i] = O[row l16][d = db*16 + 4g + i]
 #pragma unroll
@@ -381,7 +398,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
     if (!active[j]) continue;
     const float l_tot = group4_sum(l_run[j]);
     if (!rvalid[j]) continue;
-    const int r = row_lo + (wave * RBW + j) * 16 + l16;
+    const int r = row_lo + (j * kWaves + wave) * 16 + l16;
     if (P.nsplit == 1) {
       const int node = r / P.G;
       const int hq = h * P.G + (r - node * P.G);
