@@ -579,7 +579,7 @@ __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H,
 }
 
 // ------------------------------------------------------ packed W, wide tiles
-// Past 128 hidden rows the product leaves the HBM bound: at M = 960 it needs
+// Past 64 hidden rows the product leaves the HBM bound: at M = 960 it needs
 // 0.49 ms of bf16 MFMA at the dense peak against 0.16 ms to stream W.  The
 // 64-row kernel above would re-read every W image once per 64 rows, and its
 // 16 x 64 wave tiles spend more LDS bandwidth than MFMA time.  Here a
@@ -901,10 +901,11 @@ size_t lmhead_fused_ws_bytes(int M, int V, int k) {
 namespace {
 int packed_tiles_m(int M) { return (M + BM - 1) / BM; }
 int wide_tiles_m(int M) { return (M + WD_BM - 1) / WD_BM; }
-// The fused packed path takes the wide tiles above 128 rows.  Up to 128
-// rows the product is bound by streaming W, and the 64-row kernel (its m
-// tiles sharing each image through L2) streams it faster.
-bool packed_wide(int M) { return M > 2 * BM; }
+// The fused packed path takes the wide tiles above 64 rows (65-128 rows:
+// one m tile, each W image read once; the 64-row kernel would run two m
+// tiles sharing each image through L2, about 3% slower).  Up to 64 rows
+// the 64-row kernel's 8 wavefronts stream W faster than 4.
+bool packed_wide(int M) { return M > BM; }
 size_t packed_fused_ws_bytes(int M, int k) {
   const int T = packed_wide(M) ? wide_tiles_m(M) : packed_tiles_m(M);
   if (packed_tiles_m(M) > PK_GRID) return 0;
