@@ -213,6 +213,35 @@ def test_fused_packed_topk_equals_split(api, M, H, V, k):
     assert np.array_equal(vals.cpu().numpy(), ev)
 
 
+@pytest.mark.parametrize("M,k", [(40, 8), (40, 16), (100, 8), (300, 8), (300, 16)])
+def test_fused_packed_topk_ties_go_to_lower_id(api, M, k):
+    """W built from 50 distinct rows, so every logit row holds long runs of
+    bit-identical values: the fused packed top-k (64-row kernel up to 64
+    rows, wide tiles above) must rank equal logits by ascending id, exactly
+    as the oracle ranks the materialised logits."""
+    H, V = 256, 3000
+    say(f"[fused packed ties] M={M} k={k}")
+    r = np.random.default_rng(M * 3 + k)
+    base = f32_to_bf16_bits((0.05 * r.standard_normal((50, H))).astype(np.float32))
+    w = base[r.integers(0, 50, V)]
+    h = f32_to_bf16_bits(r.standard_normal((M, H)).astype(np.float32))
+    hd = dev_bf16(h)
+    wd, wp = _packed(api, w, V, H)
+    logits = torch.empty(M, V, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(api.graft_lmhead_topk_workspace_bytes(M, V, k), 1), dtype=torch.uint8, device="cuda")
+    api.graft_lmhead_topk(M, H, V, 0, hd, wd, logits)
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    vals = torch.empty(M, k, dtype=torch.float32, device="cuda")
+    api.graft_lmhead_topk(M, H, V, k, hd, wp, None, ids, vals, ws, w_layout=1)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    eid, ev = OT.topk(lg, k)
+    # the rows really are tied: each row's best value occurs many times
+    assert all(np.count_nonzero(lg[i] == lg[i].max()) >= 20 for i in range(M))
+    assert np.array_equal(ids.cpu().numpy(), eid)
+    assert np.array_equal(vals.cpu().numpy(), ev)
+
+
 # ----------------------------------------------------------------------------- sampling (T > 0)
 
 @pytest.mark.parametrize("T", [0.6, 1.0, 1.7])
@@ -271,7 +300,7 @@ def test_draws_round_twice_not_fused(api, T):
 
 
 @pytest.mark.parametrize("M,H,V,k,T", [(60, 4096, 128256, 8, 1.0), (130, 384, 1001, 16, 0.7), (1, 128, 5, 3, 2.0),
-                                       (2112, 128, 300, 8, 1.0)])
+                                       (2112, 128, 300, 8, 1.0), (68, 512, 4001, 8, 1.3), (200, 256, 3000, 8, 0.9)])
 def test_fused_sampling_equals_split(api, M, H, V, k, T):
     """The fused lm-head draws exactly what graft_sample_rows (and the
     oracle, in the same fp32 operations) draws on the logits the split mode
@@ -301,6 +330,47 @@ def test_fused_sampling_equals_split(api, M, H, V, k, T):
     eid, ev = OT.topk(lg, k)
     assert np.array_equal(ids.cpu().numpy(), eid)
     assert np.array_equal(vals.cpu().numpy(), ev)
+
+
+@pytest.mark.parametrize("M,T", [(40, 0.7), (100, 1.3)])
+def test_fused_draws_round_twice_not_fused(api, M, T):
+    """The fused lm-head's draw (one and two 64-row m tiles) rounds
+    l * (1/T) and then + g, as the definition states.  One-hot
+    hidden rows make logit (m, 0) exactly the bf16 weight W[0, m] and logit
+    (m, 1) exactly 0; each row's noise makes entry 1 tie entry 0 under two
+    roundings (id 0 wins) but not under a fused multiply-add."""
+    from fractions import Fraction
+    H, V = 128, 2
+    r = np.random.default_rng(977 + M)
+    inv = np.float32(1.0) / np.float32(T)
+    l0s, gs = [], []
+    while len(l0s) < M:
+        bits = f32_to_bf16_bits(np.array([r.standard_normal() * 3], np.float32))
+        l0 = (bits.astype(np.uint32) << 16).view(np.float32)[0]
+        g0 = np.float32(r.standard_normal() * 3)
+        two = np.float32(np.float32(l0 * inv) + g0)
+        fused = np.float32(float(Fraction(float(l0)) * Fraction(float(inv)) + Fraction(float(g0))))
+        if fused == two:
+            continue
+        l0s.append(l0)
+        gs.append([g0, two])
+    h = np.zeros((M, H), np.uint16)
+    h[np.arange(M), np.arange(M)] = 0x3F80  # bf16 1.0
+    w = np.zeros((V, H), np.uint16)
+    w[0, :M] = f32_to_bf16_bits(np.array(l0s, np.float32))
+    hd = dev_bf16(h)
+    _, wp = _packed(api, w, V, H)
+    g = np.array(gs, np.float32)
+    gd = torch.from_numpy(g).cuda()
+    ws = torch.empty(api.graft_lmhead_sample_workspace_bytes(M, V, 1), dtype=torch.uint8, device="cuda")
+    ids = torch.empty(M, 1, dtype=torch.int32, device="cuda")
+    samp = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+    api.graft_lmhead_topk_sample(M, H, V, 1, T, hd, wp, gd, ids, None, samp, ws)
+    torch.cuda.synchronize()
+    lg = np.stack([np.array(l0s, np.float32), np.zeros(M, np.float32)], axis=1)
+    exp = OS.sample_rows(lg, T, g)
+    assert exp.tolist() == [0] * M
+    assert samp.cpu().numpy().tolist() == exp.tolist()
 
 
 def _tree_with_duplicate_siblings(r, n, V):
