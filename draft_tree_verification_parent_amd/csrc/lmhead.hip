@@ -591,15 +591,14 @@ __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H,
 // completion) the CU takes in about 30-35 GB/s, hits and misses alike.
 //
 // The ring stages 64 hidden columns at a time, one packed image per 128
-// vocabulary rows (3 x 48 KB for BV = 256).  In LDS a row takes 128 bytes:
-// row r sits at line r ^ ((r >> 3) & 1) with its 16-byte pieces
-// XOR-swizzled by (r % 8), so any 8 lanes of a fragment read (rows r0 ..
-// r0 + 7) hit 8 different 16-byte bank groups of a 128-byte span, and any
-// 16 (rows r0 .. r0 + 15) 16 different ones of a 256-byte span.  Each DMA
-// instruction fills eight lines from eight consecutive rows of one image
-// (1 KB of contiguous source), so the image index is a scalar; the last
-// tile's second image is clamped to the last image (its rows are all past
-// V).
+// vocabulary rows (3 x 48 KB for BV = 256).  In LDS row r takes the 128
+// bytes at r * 128 with its 16-byte pieces XOR-swizzled by (r % 8): the
+// fragment reads measure 0.03 bank conflicts per access (rocprofv3
+// LdsBankConflict; swapping the parity of rows r and r + 8 as well, which
+// spreads 16 rows over all 64 banks on paper, measured 0.96).  Each DMA
+// instruction fills eight rows of one image from 1 KB of contiguous
+// source, so the image index is a scalar; the last tile's second image is
+// clamped to the last image (its rows are all past V).
 //
 // Epilogue (per tile): the stage of the tile's last chunk is free until the
 // next ring barrier; the 128 x BV logits go through it in 4 passes of 32
@@ -620,7 +619,7 @@ __device__ inline const unsigned char *wd_uniform(const unsigned char *p) {
 }
 
 // LDS byte offset of logical piece P (8 bf16) of row r in a stage region
-__device__ inline int wd_piece(int r, int P) { return ((r ^ ((r >> 3) & 1)) << 7) + ((P ^ (r & 7)) << 4); }
+__device__ inline int wd_piece(int r, int P) { return (r << 7) + ((P ^ (r & 7)) << 4); }
 
 // Wait until at most n * D of this wave's DMAs are outstanding (n <= NMAX,
 // picked at run time; vmcnt takes an immediate), then meet the other waves.
@@ -673,21 +672,19 @@ __global__ __launch_bounds__(256, 1) void lmhead_wide_kernel(int M, int H, int V
   const int wm = wave >> 1, wv = wave & 1;
   const unsigned sbase = static_cast<unsigned>(reinterpret_cast<size_t>((__attribute__((address_space(3))) void *)sm));
 
-  // DMA source offsets: lane -> (line, slot) -> (row, logical piece) ->
-  // its place in the row-major packed image (W) or the row-major hidden
-  // state (rows clamped to M - 1).  The line -> row map is its own inverse.
+  // DMA source offsets: lane -> (row, slot) -> logical piece -> its place
+  // in the row-major packed image (W) or the row-major hidden state (rows
+  // clamped to M - 1).
   unsigned wo[WI], ho[HI];
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
-    const int L = 8 * (wave * WI + i) + (lane >> 3);
-    const int r = L ^ ((L >> 3) & 1);
+    const int r = 8 * (wave * WI + i) + (lane >> 3);
     const int P = (lane & 7) ^ (r & 7);
     wo[i] = static_cast<unsigned>((r & (PK_BV - 1)) * 128 + (P << 4));
   }
 #pragma unroll
   for (int i = 0; i < HI; ++i) {
-    const int L = 8 * (wave * HI + i) + (lane >> 3);
-    const int r = L ^ ((L >> 3) & 1);
+    const int r = 8 * (wave * HI + i) + (lane >> 3);
     const int P = (lane & 7) ^ (r & 7);
     const int m = min(m0 + r, M - 1);
     ho[i] = static_cast<unsigned>(m) * H * 2 + (P << 4);
