@@ -272,6 +272,15 @@ def main():
                              "hbm_frac": round(kv_bytes / (kv_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 6),
                              "note": "round chaining step, timed on its own (not in the round)"}
 
+    # Tree attention warm: back-to-back calls on the same inputs, so the KV
+    # is served from the 256 MB Infinity Cache when it fits there.  In the
+    # round it is cold: the lm-head's weight stream evicts it between calls.
+    att_warm = graph_us(vr.step_tree_attention, args.steps)
+    kernels["tree_attention"].update({
+        "us_warm": round(att_warm, 2),
+        "note": "us: in the round (cold caches: the lm-head's weight stream evicts the KV between calls); "
+                "us_warm: back-to-back calls"})
+
     # Sampling at T = 1 (graft_lmhead_topk_sample: top-k plus one Gumbel-max
     # draw per row in the same pass over W; the noise is an input, 4 B per
     # logit), timed on its own in a graph of calls beside the greedy pass.
