@@ -123,6 +123,21 @@ def test_workspace_sizes(native):
     assert L.graft_lmhead_topk_workspace_bytes(60, 1000, 8) >= 60 * 256 * 8 * 8
     assert L.graft_lmhead_topk_workspace_bytes(60, 128256, 8) > 0
     assert L.graft_lmhead_topk_workspace_bytes(0, 128256, 8) == 0
+
+    # the fused packed path keeps one k-key list per (row, vocabulary stream):
+    # up to 64 rows one 64-row m tile, above that 128-row tiles; T m tiles
+    # share the 256 persistent workgroups as 32 // T groups per XCD (T <= 32)
+    # or 256 // T streams
+    def streams(T):
+        return (32 // T) * 8 if T <= 32 else 256 // T
+
+    for M in (1, 60, 64, 65, 128, 129, 960, 2112):
+        for k in (1, 8, 16):
+            T = -(-M // 64) if M <= 64 else -(-M // 128)
+            assert L.graft_lmhead_topk_workspace_bytes(M, 151936, k) >= M * streams(T) * k * 8, (M, k)
+            # sampling: 64-row m tiles at every M, k keys plus one draw key per list
+            T64 = -(-M // 64)
+            assert L.graft_lmhead_sample_workspace_bytes(M, 151936, k) == M * streams(T64) * (k + 1) * 8, (M, k)
     # tiny single-split attention needs no workspace; long context does
     assert L.graft_tree_attention_workspace_bytes(1, 4, 2, 64, 100, 15) == 0
     assert L.graft_tree_attention_workspace_bytes(1, 32, 8, 128, 32768, 63) > 0
