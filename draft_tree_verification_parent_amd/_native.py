@@ -43,7 +43,7 @@ SIGNATURES = {
 }
 
 GRAFT_OK, GRAFT_EINVAL, GRAFT_EUNSUPPORTED, GRAFT_EHIP = 0, -1, -2, -3
-ERR_TOKEN, ERR_PARENT, ERR_NOT_CLOSED, ERR_CAPACITY, ERR_RANK = 1, 2, 4, 8, 16
+ERR_TOKEN, ERR_PARENT, ERR_NOT_CLOSED, ERR_CAPACITY, ERR_RANK, ERR_ALIGN = 1, 2, 4, 8, 16, 32
 SRC_ROOT, SRC_DRAFT, SRC_RETRIEVED, SRC_REPLACED = 0, 1, 2, 3
 TREE_PRUNE, TREE_STATIC_REPLACE, TREE_TAIL = 0, 1, 2
 W_ROWMAJOR, W_PACKED = 0, 1

@@ -152,7 +152,10 @@ __device__ inline bool request_ok(const Params &P, int b, int &ctx, int &n) {
   const bool ok = ctx >= 0 && ctx <= P.max_ctx && n >= 1 && n <= P.max_n && n <= GRAFT_MAX_NODES &&
                   n <= ld_scalar(P.row_off + b + 1) - ld_scalar(P.row_off + b);
   if (!ok && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) graft::raise_flag(P.err, GRAFT_ERR_CAPACITY);
-  return ok;
+  // K/V rows are copied 16 bytes at a time from kv_off[b] on
+  const bool aligned = (ld_scalar(P.kv_off + b) & 7) == 0;
+  if (!aligned && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) graft::raise_flag(P.err, GRAFT_ERR_ALIGN);
+  return ok && aligned;
 }
 
 template <int D, int RBW, int NS>
@@ -563,6 +566,10 @@ extern "C" int graft_tree_attention(int B, int Hq, int Hkv, int d, float scale, 
   if (B == 0) return GRAFT_OK;
   if (!q || !kcache || !vcache || !kv_off || !ctx_len || !n || !row_off || !mask || !out)
     return fail(GRAFT_EINVAL, "tree_attention: NULL array");
+  if (!graft::aligned16(q) || !graft::aligned16(kcache) || !graft::aligned16(vcache) || !graft::aligned16(out) ||
+      kv_head_stride % 8 != 0)
+    return fail(GRAFT_EINVAL, "tree_attention: q, kcache, vcache and out must be 16-byte aligned and "
+                              "kv_head_stride a multiple of 8");
   if (kv_head_stride < static_cast<int64_t>(max_ctx + max_n) * d)
     return fail(GRAFT_EINVAL, "tree_attention: kv_head_stride %lld < (max_ctx + max_n) * d",
                 static_cast<long long>(kv_head_stride));

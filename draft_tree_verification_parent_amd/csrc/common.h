@@ -17,6 +17,9 @@ int check_launch(const char *what);
 void clear_error();
 
 inline hipStream_t as_stream(graft_stream s) { return reinterpret_cast<hipStream_t>(s); }
+// Arrays the kernels read or write 16 bytes at a time must start on a
+// 16-byte boundary (every PyTorch allocation does).
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ORs error bits into the caller's device flag word (vector-memory atomic).
 __device__ inline void raise_flag(int32_t *err, int bits) {

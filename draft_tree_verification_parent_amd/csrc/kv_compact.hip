@@ -49,11 +49,13 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(
     const bool step_ok = tid > a || (tid == 0 ? p == 0 : (p > prev && p < n));
     const bool path_ok = len_ok && __builtin_amdgcn_ballot_w64(!step_ok) == 0;
     const bool fits = ctx >= 0 && n >= 1 && static_cast<int64_t>(ctx) + n <= cap;
+    const bool aligned = (kv_off[b] & 7) == 0;  // rows move 16 bytes at a time
     s_path[tid] = p;
     if (tid == 0) {
-      s_ok = path_ok && fits;
+      s_ok = path_ok && fits && aligned;
       if (lead && !path_ok) graft::raise_flag(err, GRAFT_ERR_PARENT);
       if (lead && path_ok && !fits) graft::raise_flag(err, GRAFT_ERR_CAPACITY);
+      if (lead && !aligned) graft::raise_flag(err, GRAFT_ERR_ALIGN);
     }
   }
   __syncthreads();
@@ -119,6 +121,8 @@ extern "C" int graft_kv_compact(int B, int Hkv, int d, int n_layers, graft_bf16 
   if (!kcache || !vcache || !kv_off || !ctx_len || !n || !acc_len || !acc_path || !bonus || !ctx_next || !root_next)
     return fail(GRAFT_EINVAL, "kv_compact: NULL array");
   if (ctx_next == ctx_len) return fail(GRAFT_EINVAL, "kv_compact: ctx_next must not alias ctx_len");
+  if (!graft::aligned16(kcache) || !graft::aligned16(vcache) || (n_layers > 1 && layer_stride % 8 != 0))
+    return fail(GRAFT_EINVAL, "kv_compact: kcache and vcache must be 16-byte aligned, layer_stride a multiple of 8");
   graft::clear_error();
   const dim3 grid(Hkv, n_layers, B);
   if (d == 128)

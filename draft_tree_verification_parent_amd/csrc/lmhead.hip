@@ -920,6 +920,8 @@ extern "C" int graft_lmhead_pack(int V, int H, const graft_bf16 *w, graft_bf16 *
   if (V <= 0 || H <= 0 || H % PK_KC != 0)
     return fail(GRAFT_EINVAL, "lmhead_pack: V=%d H=%d (H must be a positive multiple of %d)", V, H, PK_KC);
   if (!w || !w_packed) return fail(GRAFT_EINVAL, "lmhead_pack: NULL array");
+  if (!graft::aligned16(w) || !graft::aligned16(w_packed))
+    return fail(GRAFT_EINVAL, "lmhead_pack: w and w_packed must be 16-byte aligned");
   graft::clear_error();
   const size_t pieces = graft_lmhead_pack_bytes(V, H) / 16;
   const size_t blocks = (pieces + 255) / 256;
@@ -959,6 +961,8 @@ extern "C" int graft_lmhead_topk(int M, int H, int V, int k, const graft_bf16 *h
   if (hidden && packed && static_cast<size_t>(M) * H * 2 > 0xFFFFFFFFull)
     return fail(GRAFT_EINVAL, "lmhead_topk: hidden of %d x %d exceeds 4 GiB (32-bit DMA offsets)", M, H);
   if (M == 0) return GRAFT_OK;
+  if ((hidden && !graft::aligned16(hidden)) || (hidden && !graft::aligned16(w)) || (logits && !graft::aligned16(logits)))
+    return fail(GRAFT_EINVAL, "lmhead_topk: hidden, w and logits must be 16-byte aligned");
   const bool fused = hidden && !logits;
   size_t need = k > 0 && !fused ? graft::topk_plan(M, V, k).ws_bytes : 0;
   if (fused) need = packed ? packed_fused_ws_bytes(M, k) : graft::lmhead_fused_ws_bytes(M, V, k);
@@ -1084,6 +1088,8 @@ extern "C" int graft_lmhead_topk_sample(int M, int H, int V, int k, float temper
   if (M == 0) return GRAFT_OK;
   if (!hidden || !w_packed || !gumbel || !topk_id || !sample_id)
     return fail(GRAFT_EINVAL, "lmhead_topk_sample: NULL array");
+  if (!graft::aligned16(hidden) || !graft::aligned16(w_packed) || !graft::aligned16(gumbel))
+    return fail(GRAFT_EINVAL, "lmhead_topk_sample: hidden, w_packed and gumbel must be 16-byte aligned");
   const size_t need = packed_sample_ws_bytes(M, k);
   if (ws_bytes < need || !ws) return fail(GRAFT_EINVAL, "lmhead_topk_sample: workspace %zu bytes < %zu", ws_bytes, need);
   graft::clear_error();

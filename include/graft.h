@@ -43,6 +43,12 @@
  *    and its node i (i < n[b]) is row row_off[b] + i.  row_off is
  *    non-decreasing.  Parent indices are request-local (root = node 0,
  *    parent -1).
+ *  - Arrays of bf16 or fp32 values that a kernel moves 16 bytes at a time
+ *    (hidden states, weights, logits, noise, Q, K/V caches, attention
+ *    output) must be 16-byte aligned, and K/V offsets and strides
+ *    multiples of 8 elements; every PyTorch allocation is aligned.  A
+ *    misaligned pointer or stride returns GRAFT_EINVAL; a misaligned kv_off
+ *    entry (device data) raises GRAFT_ERR_ALIGN and skips that request.
  *  - Integer results are exact; ties in any ranking go to the lower index.
  *  - bf16 tensors are raw bfloat16 bit patterns (uint16).
  */
@@ -79,6 +85,8 @@ typedef void *graft_stream;
 #define GRAFT_ERR_CAPACITY 8   /* tree larger than its rows or 64 nodes, or a
                                   length above the bound given to the call */
 #define GRAFT_ERR_RANK 16      /* template rank outside [0, k) */
+#define GRAFT_ERR_ALIGN 32     /* a K/V base offset (kv_off) not a multiple of
+                                  8 elements */
 
 /* node source codes written by graft_build_tree */
 #define GRAFT_SRC_ROOT 0

@@ -218,3 +218,34 @@ def test_treegraft_host_helper_and_validation(native):
     assert L.graft_treegraft_build(2, 5, 0, 10, p, p, p, p, p, p, p, p, p, None, None) == E
     assert L.graft_treegraft_build(2, 5, 10, 10, p, p, None, p, p, p, p, p, p, None, None) == E
     assert L.graft_treegraft_build(0, 5, 10, 10, None, None, None, None, None, None, None, None, None, None, None) == 0
+
+
+def test_misaligned_arrays_are_rejected_before_any_launch(native):
+    """Arrays the kernels move 16 bytes at a time must be 16-byte aligned,
+    K/V strides multiples of 8 elements: otherwise GRAFT_EINVAL, nothing
+    launched (the addresses below are never dereferenced)."""
+    L = native.lib()
+    E = native.GRAFT_EINVAL
+    A, X = 1 << 20, (1 << 20) + 8  # aligned / 8 bytes off
+    ws = 1 << 40
+    # lm-head: hidden, w, logits
+    for h, w, lg in ((X, A, A), (A, X, A), (A, A, X)):
+        assert L.graft_lmhead_topk(4, 256, 100, 4, h, w, 0, lg, A, A, A, ws, None) == E
+        assert b"16-byte aligned" in L.graft_last_error()
+    assert L.graft_lmhead_pack(100, 256, X, A, None) == E
+    assert L.graft_lmhead_pack(100, 256, A, X, None) == E
+    for h, w, g in ((X, A, A), (A, X, A), (A, A, X)):
+        assert L.graft_lmhead_topk_sample(4, 256, 100, 4, 1.0, h, w, g, A, A, A, A, ws, None) == E
+    # tree attention: q, kcache, vcache, out, and the head stride
+    def att(q=A, k=A, v=A, out=A, stride=4096 * 128):
+        return L.graft_tree_attention(1, 8, 2, 128, 0.1, q, k, v, A, stride, A, 4000, A, 60, A, A, out, None, A,
+                                      ws, A, None)
+    for kw in ({"q": X}, {"k": X}, {"v": X}, {"out": X}, {"stride": 4096 * 128 + 4}):
+        assert att(**kw) == E, kw
+    # KV compaction: caches and the layer stride
+    def kvc(k=A, v=A, layers=1, layer_stride=0):
+        return L.graft_kv_compact(1, 8, 128, layers, k, v, layer_stride, A, 4096 * 128, A, A, A, A, A, A + 64,
+                                  A + 128, A, None)
+    assert kvc(k=X) == E
+    assert kvc(v=X) == E
+    assert kvc(layers=2, layer_stride=8 * 4096 * 128 + 4) == E

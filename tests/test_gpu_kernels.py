@@ -23,7 +23,7 @@ from _gpu_round import say, within_tol
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-ERR_TOKEN, ERR_PARENT, ERR_NOT_CLOSED, ERR_CAPACITY, ERR_RANK = 1, 2, 4, 8, 16
+ERR_TOKEN, ERR_PARENT, ERR_NOT_CLOSED, ERR_CAPACITY, ERR_RANK, ERR_ALIGN = 1, 2, 4, 8, 16, 32
 
 
 @pytest.fixture(scope="module")
@@ -972,6 +972,51 @@ def test_attention_cases(api, B, Hq, Hkv, d, ctxs, ns):
 
 def test_attention_chain_tree(api):
     _attn_case(api, 1, 8, 2, 128, [777], [64], seed=5, chain=True)
+
+
+def test_attention_misaligned_kv_offset_is_flagged(api):
+    """A request whose kv_off is not a multiple of 8 elements is skipped and
+    flagged (its K/V would be copied 16 bytes at a time from a misaligned
+    address); the other request's output is the same as with both aligned."""
+    B, Hq, Hkv, d, cap = 2, 4, 2, 64, 300
+    r = np.random.default_rng(55)
+    q = dev_bf16(f32_to_bf16_bits(r.standard_normal((8, Hq, d)).astype(np.float32)))
+    kc = dev_bf16(f32_to_bf16_bits(r.standard_normal(2 * Hkv * cap * d + 16).astype(np.float32)))
+    vc = dev_bf16(f32_to_bf16_bits(r.standard_normal(2 * Hkv * cap * d + 16).astype(np.float32)))
+    ws = torch.empty(max(api.graft_tree_attention_workspace_bytes(B, Hq, Hkv, d, 200, 4), 1),
+                     dtype=torch.uint8, device="cuda")
+    mask = torch.from_numpy(np.array([1, 3, 5, 9, 1, 3, 7, 15], np.uint64).view(np.int64)).cuda()
+    outs, errs = [], []
+    for off1 in (Hkv * cap * d + 8, Hkv * cap * d + 4):
+        out = torch.zeros(8, Hq, d, dtype=torch.bfloat16, device="cuda")
+        err = err_buf()
+        kv_off = torch.tensor([0, off1], dtype=torch.int64, device="cuda")
+        api.graft_tree_attention(Hq, Hkv, d, 0.125, q, kc, vc, kv_off, cap * d, dev_i32([150, 120]), 200,
+                                 dev_i32([4, 4]), 4, dev_i32([0, 4, 8]), mask, out, None, ws, err)
+        torch.cuda.synchronize()
+        outs.append(out.cpu())
+        errs.append(err.item())
+    assert errs == [0, ERR_ALIGN]
+    assert torch.equal(outs[0][:4], outs[1][:4])
+
+
+def test_kv_compact_misaligned_kv_offset_is_flagged(api):
+    """kv_compact leaves a request with a misaligned kv_off untouched (context
+    not advanced, no root) and flags it."""
+    d, cap = 64, 200
+    kc = torch.zeros(cap * d + 16, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros(cap * d + 16, dtype=torch.bfloat16, device="cuda")
+    path = np.full(64, -1, np.int32)
+    path[:3] = [0, 1, 3]
+    ctx_next = dev_i32([0])
+    root_next = dev_i32([0])
+    err = err_buf()
+    api.graft_kv_compact(1, d, kc, vc, torch.tensor([4], dtype=torch.int64, device="cuda"), cap * d,
+                         dev_i32([100]), dev_i32([5]), dev_i32([2]), dev_i32(path), dev_i32([7]), ctx_next,
+                         root_next, err=err)
+    torch.cuda.synchronize()
+    assert err.item() == ERR_ALIGN
+    assert ctx_next.item() == 100 and root_next.item() == -1
 
 
 def test_attention_length_above_bound_is_flagged(api):
