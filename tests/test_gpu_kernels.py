@@ -190,7 +190,8 @@ def test_lmhead_packed_equals_rowmajor(api, M, H, V):
                                      (64, 256, 129, 10), (300, 128, 2000, 16), (2112, 128, 300, 8),
                                      (68, 1024, 5000, 8), (65, 256, 130, 16), (960, 512, 4001, 8),
                                      (129, 256, 777, 10), (200, 128, 257, 16), (384, 128, 1023, 8),
-                                     (4200, 128, 300, 8)])
+                                     (4200, 128, 300, 8), (65, 128, 1, 1), (100, 128, 60, 1), (256, 256, 511, 3),
+                                     (257, 128, 129, 16)])
 def test_fused_packed_topk_equals_split(api, M, H, V, k):
     """Packed fused top-k (lists kept per workgroup across tiles) ranks
     exactly the logits the split row-major mode writes.  Up to 64 rows one
