@@ -358,8 +358,9 @@ __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H,
   // W images stream through L2 non-temporally unless several m tiles
   // (workgroups of one XCD) read each image
   const bool w_nt = tiles_m == 1;
-  // loop-invariant DMA source offsets: W images are copied linearly; hidden
-  // row r (clamped to M - 1) lands swizzled like the images
+  // loop-invariant DMA source offsets: each instruction fills four
+  // 256-byte LDS rows, gathering their pieces from the chunk's two packed
+  // images; hidden row r (clamped to M - 1) lands swizzled the same way
   unsigned wo[WI], ho[HI];
 #pragma unroll
   for (int i = 0; i < WI; ++i) {
