@@ -7,7 +7,8 @@
 //
 // Two passes, both bound by the read of the logits:
 //  1. grid (slices, rows): each thread keeps a sorted top-K list in
-//     registers over its strided part of a slice (coalesced float4 reads),
+//     registers over its strided part of a slice (coalesced float4 reads,
+//     filtered by a wave-wide bound so that few entries are inserted),
 //     each wavefront merges its 64 lists with k rounds of a (value, id)
 //     butterfly max, and wave 0 merges the four wave results; k candidates
 //     per (row, slice) go to the workspace.
@@ -45,16 +46,79 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
 
   TopKeys<K> L;
   L.init();
+  // An entry below a value that K distinct entries of the wave reach cannot
+  // be in the top k <= K.  `bound` (a value order) is the K-th largest of the
+  // 64 lanes' list heads after each batch, and of the lanes' maxima before
+  // the first: it follows the wave's own K-th largest entry, so after the
+  // first batches almost every entry fails this one compare and a batch's
+  // 16 slots rarely run an insert.  (A uniform trip count keeps all 64 lanes
+  // in the cross-lane max.)
+  uint32_t bound = 0;
+  constexpr int U = 4;  // 16-byte loads per thread per batch, issued together
   if ((V & 3) == 0) {
-    for (int c = lo + tid * 4; c < hi; c += kThreads * 4) {
-      const float4 x = *reinterpret_cast<const float4 *>(row + c);
-      L.insert(graft::rank_key(x.x, c));
-      L.insert(graft::rank_key(x.y, c + 1));
-      L.insert(graft::rank_key(x.z, c + 2));
-      L.insert(graft::rank_key(x.w, c + 3));
+    for (int base = lo; base < hi; base += kThreads * 4 * U) {
+      float4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = base + (u * kThreads + tid) * 4;
+        x[u] = c < hi ? *reinterpret_cast<const float4 *>(row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      if (base == lo) {
+        // first batch (uniform): the K-th largest of the 64 lane maxima, so
+        // the first inserts are already filtered
+        uint32_t lm = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = base + (u * kThreads + tid) * 4;
+          const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t o = c + e < hi ? graft::float_order(xs[e]) : 0u;
+            lm = o > lm ? o : lm;
+          }
+        }
+        bound = graft::wave_kth_u32<K>(lm);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = base + (u * kThreads + tid) * 4;
+        const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < hi && graft::float_order(xs[e]) >= bound) L.insert(graft::rank_key(xs[e], c + e));
+      }
+      // each lane's list head is its largest entry: K lanes hold an entry
+      // at least the K-th largest head
+      const uint32_t lb = graft::wave_kth_u32<K>(static_cast<uint32_t>(L.k[0] >> 32));
+      bound = lb > bound ? lb : bound;
     }
   } else {
-    for (int c = lo + tid; c < hi; c += kThreads) L.insert(graft::rank_key(row[c], c));
+    for (int base = lo; base < hi; base += kThreads * U) {
+      float x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = base + u * kThreads + tid;
+        x[u] = c < hi ? row[c] : 0.f;
+      }
+      if (base == lo) {
+        uint32_t lm = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t o = base + u * kThreads + tid < hi ? graft::float_order(x[u]) : 0u;
+          lm = o > lm ? o : lm;
+        }
+        bound = graft::wave_kth_u32<K>(lm);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = base + u * kThreads + tid;
+        if (c < hi && graft::float_order(x[u]) >= bound) L.insert(graft::rank_key(x[u], c));
+      }
+      // each lane's list head is its largest entry: K lanes hold an entry
+      // at least the K-th largest head
+      const uint32_t lb = graft::wave_kth_u32<K>(static_cast<uint32_t>(L.k[0] >> 32));
+      bound = lb > bound ? lb : bound;
+    }
   }
 
   uint64_t r = graft::wave_extract<K>(L, k);

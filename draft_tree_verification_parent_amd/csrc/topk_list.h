@@ -92,6 +92,34 @@ __device__ inline uint64_t group_max(uint64_t x) {
   return x;
 }
 
+// Largest 32-bit value over the 64 lanes of a wavefront (every lane gets it).
+__device__ inline uint32_t wave_max_u32(uint32_t x) {
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  x = mx(x, lanes::dpp<lanes::kXor1>(x));
+  x = mx(x, lanes::dpp<lanes::kXor2>(x));
+  x = mx(x, lanes::dpp<lanes::kHalfMirror>(x));
+  x = mx(x, lanes::dpp<lanes::kMirror>(x));
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = mx(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return mx(b[0], b[1]);
+}
+
+// The K-th largest of the 64 lanes' values (0 = none): K rounds of
+// remove-the-largest; lanes holding an equal maximum are removed together,
+// which only lowers the result.
+template <int K>
+__device__ inline uint32_t wave_kth_u32(uint32_t v) {
+  uint32_t kth = 0;
+#pragma unroll
+  for (int r = 0; r < K; ++r) {
+    const uint32_t b = wave_max_u32(v);
+    v = v == b ? 0u : v;
+    kth = b;
+  }
+  return kth;
+}
+
 // Largest float over aligned groups of W <= 8 lanes (every lane of the group gets it).
 template <int W>
 __device__ inline float group_maxf(float x) {
