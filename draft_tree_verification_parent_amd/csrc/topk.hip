@@ -140,8 +140,10 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
   }
 }
 
-// One 256-thread workgroup per row: each thread ranks ~1/256 of the row's
-// candidates (loads batched 8 at a time so their latencies overlap), each
+// One 256-thread workgroup per row.  With at most 256 candidate lists a
+// thread takes one list as its own sorted list (the producers write each
+// list largest first); otherwise each thread ranks ~1/256 of the row's
+// candidates (loads batched 8 at a time so their latencies overlap).  Each
 // wavefront extracts its k best, and wave 0 merges the four wave results.
 template <int K>
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(int S, int k, const uint64_t *__restrict__ part,
@@ -156,16 +158,26 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(int S, int k, cons
   const int n = S * k;
   TopKeys<K> L;
   L.init();
-  constexpr int BATCH = 8;
-  for (int c0 = 0; c0 < n; c0 += kThreads * BATCH) {
-    uint64_t x[BATCH];
+  if (S <= kThreads) {
+    // every producer writes its k keys sorted (largest first): thread t
+    // takes list t as its own, no inserts needed
+    if (tid < S) {
+      const uint64_t *lst = row + static_cast<size_t>(tid) * k;
 #pragma unroll
-    for (int j = 0; j < BATCH; ++j) {
-      const int c = c0 + j * kThreads + tid;
-      x[j] = c < n ? row[c] : 0;
+      for (int j = 0; j < K; ++j) L.k[j] = j < k ? lst[j] : 0;
     }
+  } else {
+    constexpr int BATCH = 8;
+    for (int c0 = 0; c0 < n; c0 += kThreads * BATCH) {
+      uint64_t x[BATCH];
 #pragma unroll
-    for (int j = 0; j < BATCH; ++j) L.insert(x[j]);
+      for (int j = 0; j < BATCH; ++j) {
+        const int c = c0 + j * kThreads + tid;
+        x[j] = c < n ? row[c] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < BATCH; ++j) L.insert(x[j]);
+    }
   }
   uint64_t r = graft::wave_extract<K>(L, k);
   if (lane < k) s_k[wave][lane] = r;
