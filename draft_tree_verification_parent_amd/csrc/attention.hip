@@ -576,6 +576,8 @@ extern "C" int graft_tree_attention(int B, int Hq, int Hkv, int d, float scale, 
   const Plan pl = make_plan(B, Hq, Hkv, d, max_ctx, max_n);
   if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws))
     return fail(GRAFT_EINVAL, "tree_attention: workspace %zu bytes < %zu", ws_bytes, pl.ws_bytes);
+  if (pl.ws_bytes > 0 && !graft::aligned16(ws))  // partial O rows are moved 16 bytes at a time
+    return fail(GRAFT_EINVAL, "tree_attention: workspace must be 16-byte aligned");
   if (pl.nsplit > 65535 || static_cast<long long>(Hkv) * pl.row_groups > 65535 || B > 65535)
     return fail(GRAFT_EINVAL, "tree_attention: grid too large");
   graft::clear_error();

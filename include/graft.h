@@ -45,8 +45,9 @@
  *    parent -1).
  *  - Arrays of bf16 or fp32 values that a kernel moves 16 bytes at a time
  *    (hidden states, weights, logits, noise, Q, K/V caches, attention
- *    output) must be 16-byte aligned, and K/V offsets and strides
- *    multiples of 8 elements; every PyTorch allocation is aligned.  A
+ *    output, the tree-attention workspace) must be 16-byte aligned, and
+ *    K/V offsets and strides multiples of 8 elements; every PyTorch
+ *    allocation is aligned.  A
  *    misaligned pointer or stride returns GRAFT_EINVAL; a misaligned kv_off
  *    entry (device data) raises GRAFT_ERR_ALIGN and skips that request.
  *  - Integer results are exact; ties in any ranking go to the lower index.

@@ -236,11 +236,12 @@ def test_misaligned_arrays_are_rejected_before_any_launch(native):
     assert L.graft_lmhead_pack(100, 256, A, X, None) == E
     for h, w, g in ((X, A, A), (A, X, A), (A, A, X)):
         assert L.graft_lmhead_topk_sample(4, 256, 100, 4, 1.0, h, w, g, A, A, A, A, ws, None) == E
-    # tree attention: q, kcache, vcache, out, and the head stride
-    def att(q=A, k=A, v=A, out=A, stride=4096 * 128):
-        return L.graft_tree_attention(1, 8, 2, 128, 0.1, q, k, v, A, stride, A, 4000, A, 60, A, A, out, None, A,
-                                      ws, A, None)
-    for kw in ({"q": X}, {"k": X}, {"v": X}, {"out": X}, {"stride": 4096 * 128 + 4}):
+    # tree attention: q, kcache, vcache, out, the split workspace, and the head stride
+    def att(q=A, k=A, v=A, out=A, wsp=A, stride=4096 * 128):
+        return L.graft_tree_attention(1, 8, 2, 128, 0.1, q, k, v, A, stride, A, 4000, A, 60, A, A, out, None,
+                                      wsp, ws, A, None)
+    assert L.graft_tree_attention_workspace_bytes(1, 8, 2, 128, 4000, 60) > 0  # split, so the workspace is used
+    for kw in ({"q": X}, {"k": X}, {"v": X}, {"out": X}, {"wsp": X}, {"stride": 4096 * 128 + 4}):
         assert att(**kw) == E, kw
     # KV compaction: caches and the layer stride
     def kvc(k=A, v=A, layers=1, layer_stride=0):
