@@ -46,9 +46,7 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int KCH = 64;      // keys per staged chunk (four 16-key MFMA blocks)
-constexpr int NS_SHORT = 4;  // LDS ring stages: one 128 KB workgroup per CU
-constexpr int NS_LONG = 2;   // two 64 KB workgroups per CU (long key ranges)
-constexpr int LONG_KEYS = 16384;  // key range from which the 2-stage ring is used
+constexpr int NS = 4;        // LDS ring stages (128 KB at d = 128: one workgroup per CU)
 constexpr int MIN_SPLIT = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -158,7 +156,7 @@ __device__ inline bool request_ok(const Params &P, int b, int &ctx, int &n) {
   return ok && aligned;
 }
 
-template <int D, int RBW, int NS>
+template <int D, int RBW>
 __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
   using TL = Tile<D>;
   constexpr int DS = D / 32;  // MFMA k-steps over the head dim
@@ -248,6 +246,19 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
     for (int s = 0; s < DS; ++s) qf[j][s] = rvalid[j] ? __builtin_bit_cast(bf16x8, load16(qp + s * 32)) : zero8();
   }
 
+  // Retire the Q and mask loads here.  The compiler does not see the DMAs
+  // (they are asm), so its own wait for these loads, placed at their first
+  // use inside the ring loop, would be a vmcnt(0) run on every chunk: each
+  // chunk would wait for every DMA in flight, the ring would never overlap
+  // compute.  Used once here, they cost one wait that also covers the
+  // prologue's chunks, which the first chunk needs anyway.
+#pragma unroll
+  for (int j = 0; j < RBW; ++j) {
+    asm volatile("" ::"v"(mrow[j]));
+#pragma unroll
+    for (int s = 0; s < DS; ++s) asm volatile("" ::"v"(qf[j][s]));
+  }
+
   f32x4 oacc[RBW][DB];
   float m_run[RBW], l_run[RBW];
 #pragma unroll
@@ -282,15 +293,37 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
     for (int j = 0; j < NA; ++j)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) sacc[j][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (NA <= 2) {
+      // registers to spare: all 4 x DS K fragments are read first, in the
+      // order the MFMAs consume them, and the MFMAs run k-step by k-step
+      // over the four key blocks, so consecutive MFMAs never depend on each
+      // other and each waits only for its own fragment
+      bf16x8 kf[DS][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+      for (int s = 0; s < DS; ++s)
 #pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8 *)(
-            ks + 16 * kb * TL::ROW + kfrag + (((4 * s + g) ^ swk) * 16));
+        for (int kb = 0; kb < 4; ++kb)
+          kf[s][kb] = *(const __attribute__((address_space(3))) bf16x8 *)(ks + 16 * kb * TL::ROW + kfrag +
+                                                                          (((4 * s + g) ^ swk) * 16));
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
 #pragma unroll
-        for (int j = 0; j < NA; ++j)
-          sacc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j][s], sacc[j][kb], 0, 0, 0);
+      for (int s = 0; s < DS; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int j = 0; j < NA; ++j)
+            sacc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s][kb], qf[j][s], sacc[j][kb], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8 *)(
+              ks + 16 * kb * TL::ROW + kfrag + (((4 * s + g) ^ swk) * 16));
+#pragma unroll
+          for (int j = 0; j < NA; ++j)
+            sacc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[j][s], sacc[j][kb], 0, 0, 0);
+        }
       }
     }
     // online softmax (base 2).  A chunk that lies entirely inside the
@@ -379,6 +412,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
   constexpr int PER = 2 * DI;  // DMAs per wave per chunk
   auto run = [&](auto na_tag) {
     for (int c = 0; c < nch; ++c) {
+      static_assert(NS - 2 <= 2, "the waits below cover at most two younger chunks");
       const int younger = min(nch - 1 - c, NS - 2);  // chunks issued after c
       if (younger >= 2) ring_barrier<2 * PER>();
       else if (younger == 1) ring_barrier<PER>();
@@ -481,7 +515,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(Params P) {
 }
 
 struct Plan {
-  int rbw, ns, row_groups, rows_per_wg, rows_cap, split_len, nsplit;
+  int rbw, row_groups, rows_per_wg, rows_cap, split_len, nsplit;
   size_t ws_bytes;
 };
 
@@ -501,16 +535,14 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int max_n) {
   else if (rb <= kWaves) p.rbw = 1;
   else if (rb <= 2 * kWaves) p.rbw = 2;
   else p.rbw = 3;
-  // Long key ranges with one row block per wave use the 2-stage ring: two
-  // 64 KB workgroups share a CU and overlap each other's stalls.
-  p.ns = (p.rbw == 1 && L >= LONG_KEYS) ? NS_LONG : NS_SHORT;
   p.rows_per_wg = kWaves * p.rbw * 16;
   p.row_groups = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
   p.rows_cap = rb * 16;
-  // split the keys so that about 256 (one per CU) or 512 (two per CU)
-  // workgroups run at once
+  // split the keys so that about 256 workgroups (one per CU) run at once
+  // (128 and 512 measured slower, and so did a 2-stage ring with two
+  // workgroups per CU for long key ranges)
   const long long units = static_cast<long long>(B) * Hkv * p.row_groups;
-  const long long target = p.ns == NS_LONG ? 512 : 256;
+  const long long target = 256;
   long long want = units > 0 ? (target + units - 1) / units : 1;
   if (want < 1) want = 1;
   long long len = (L + want - 1) / want;
@@ -529,14 +561,12 @@ bool shape_ok(int B, int Hq, int Hkv, int d, int max_ctx, int max_n) {
 
 template <int D>
 void launch(const Plan &pl, const Params &P, dim3 grid, hipStream_t s) {
-  if (pl.rbw == 1 && pl.ns == NS_LONG)
-    hipLaunchKernelGGL((tree_attn_kernel<D, 1, NS_LONG>), grid, dim3(kThreads), 0, s, P);
-  else if (pl.rbw == 1)
-    hipLaunchKernelGGL((tree_attn_kernel<D, 1, NS_SHORT>), grid, dim3(kThreads), 0, s, P);
+  if (pl.rbw == 1)
+    hipLaunchKernelGGL((tree_attn_kernel<D, 1>), grid, dim3(kThreads), 0, s, P);
   else if (pl.rbw == 2)
-    hipLaunchKernelGGL((tree_attn_kernel<D, 2, NS_SHORT>), grid, dim3(kThreads), 0, s, P);
+    hipLaunchKernelGGL((tree_attn_kernel<D, 2>), grid, dim3(kThreads), 0, s, P);
   else
-    hipLaunchKernelGGL((tree_attn_kernel<D, 3, NS_SHORT>), grid, dim3(kThreads), 0, s, P);
+    hipLaunchKernelGGL((tree_attn_kernel<D, 3>), grid, dim3(kThreads), 0, s, P);
   if (pl.nsplit > 1) {
     constexpr int RPB = 256 / (D / 4);
     dim3 mg((pl.rows_cap + RPB - 1) / RPB, P.Hkv, P.B);
