@@ -142,18 +142,36 @@ __device__ inline T ld_scalar(const T *p) {
   return *(const __attribute__((address_space(4))) T *)p;
 }
 
-// Returns false (and flags once) when the request's lengths exceed the
-// bounds the grid was sized for or its row capacity.
-__device__ inline bool request_ok(const Params &P, int b, int &ctx, int &n) {
-  ctx = ld_scalar(P.ctx_len + b);
-  n = ld_scalar(P.n + b);
-  const bool ok = ctx >= 0 && ctx <= P.max_ctx && n >= 1 && n <= P.max_n && n <= GRAFT_MAX_NODES &&
-                  n <= ld_scalar(P.row_off + b + 1) - ld_scalar(P.row_off + b);
-  if (!ok && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) graft::raise_flag(P.err, GRAFT_ERR_CAPACITY);
-  // K/V rows are copied 16 bytes at a time from kv_off[b] on
-  const bool aligned = (ld_scalar(P.kv_off + b) & 7) == 0;
-  if (!aligned && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) graft::raise_flag(P.err, GRAFT_ERR_ALIGN);
-  return ok && aligned;
+// One request's scalars.
+struct Request {
+  int ctx, n, r_off;
+  int64_t kv_off;
+};
+
+// Loads the request's scalars and returns false (flagging once) when its
+// lengths exceed the bounds the grid was sized for or its row capacity, or
+// its K/V offset is not a multiple of 8 elements (K/V rows are copied 16
+// bytes at a time from kv_off[b] on).  All five loads are issued together:
+// with short-circuit tests, or a flag branch between them, each would wait
+// for the one before, a chain of round trips ahead of the first K/V copy.
+__device__ inline bool request_ok(const Params &P, int b, Request &q) {
+  q.kv_off = ld_scalar(P.kv_off + b);
+  q.ctx = ld_scalar(P.ctx_len + b);
+  q.n = ld_scalar(P.n + b);
+  q.r_off = ld_scalar(P.row_off + b);
+  const int r_end = ld_scalar(P.row_off + b + 1);
+  // one use of all five, and nothing scheduled across it: the loads are all
+  // issued before the single wait for them
+  asm volatile("" ::"s"(q.kv_off), "s"(q.ctx), "s"(q.n), "s"(q.r_off), "s"(r_end));
+  __builtin_amdgcn_sched_barrier(0);
+  const bool ok = (q.ctx >= 0) & (q.ctx <= P.max_ctx) & (q.n >= 1) & (q.n <= P.max_n) &
+                  (q.n <= GRAFT_MAX_NODES) & (q.n <= r_end - q.r_off);
+  const bool aligned = (q.kv_off & 7) == 0;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    if (!ok) graft::raise_flag(P.err, GRAFT_ERR_CAPACITY);
+    if (!aligned) graft::raise_flag(P.err, GRAFT_ERR_ALIGN);
+  }
+  return ok & aligned;
 }
 
 template <int D, int RBW>
@@ -168,8 +186,9 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
   const int h = blockIdx.y / P.row_groups;
   const int rg = blockIdx.y - h * P.row_groups;
   const int split = blockIdx.x;
-  int ctx, n;
-  if (!request_ok(P, b, ctx, n)) return;
+  Request q;
+  if (!request_ok(P, b, q)) return;
+  const int ctx = q.ctx, n = q.n;
   const int L = ctx + n;
   const int k_begin = split * P.split_len;
   if (k_begin >= L) return;
@@ -184,14 +203,14 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
   const int lane = tid & 63;
   const int l16 = lane & 15;
   const int g = lane >> 4;
-  const int r_off = ld_scalar(P.row_off + b);
+  const int r_off = q.r_off;
 
   // ---- LDS DMA ring.  Lane l of this wave's i-th K (V) instruction copies
   // piece (slot ^ swz(row)) of key row `row` of the chunk into slot `slot`.
   // Slots past k_end re-read the last valid slot (in bounds; their scores
   // are masked and their P is 0).
   const unsigned sbase = static_cast<unsigned>(reinterpret_cast<size_t>((lds_u8 *)sm));
-  const size_t kv_base = static_cast<size_t>(ld_scalar(P.kv_off + b)) + static_cast<size_t>(h) * P.head_stride;
+  const size_t kv_base = static_cast<size_t>(q.kv_off) + static_cast<size_t>(h) * P.head_stride;
   const unsigned char *kbase = uniform_ptr(reinterpret_cast<const unsigned char *>(P.kc + kv_base));
   const unsigned char *vbase = uniform_ptr(reinterpret_cast<const unsigned char *>(P.vc + kv_base));
   int drow[DI];
@@ -473,10 +492,10 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(Params P) {
   const int h = blockIdx.y;
   const int r = blockIdx.x * RPB + threadIdx.x / TPR;
   const int c = (threadIdx.x % TPR) * 4;
-  int ctx, n;
-  if (!request_ok(P, b, ctx, n)) return;
-  if (r >= n * P.G) return;
-  const int L = ctx + n;
+  Request q;
+  if (!request_ok(P, b, q)) return;
+  if (r >= q.n * P.G) return;
+  const int L = q.ctx + q.n;
   const int ns = (L + P.split_len - 1) / P.split_len;
   const size_t base = (static_cast<size_t>(b) * P.Hkv + h) * P.nsplit * P.rows_cap + r;
   float M = -INFINITY, wsum = 0.f;
@@ -505,7 +524,7 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(Params P) {
   }
   const int node = r / P.G;
   const int hq = h * P.G + (r - node * P.G);
-  const size_t orow = static_cast<size_t>(P.row_off[b] + node) * P.Hq + hq;
+  const size_t orow = static_cast<size_t>(q.r_off + node) * P.Hq + hq;
   const float inv = 1.f / wsum;
   bf16x4 ob;
 #pragma unroll
