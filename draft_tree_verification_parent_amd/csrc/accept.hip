@@ -35,9 +35,23 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t *__restrict__ 
                                                     int32_t *__restrict__ err) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
+  // Two rounds of loads in all: the request's scalars, then every node array
+  // (their addresses depend only on row_off[b]).  Each round is used once
+  // before anything else, so no test or branch splits it into a chain.
   const int r0 = row_off[b];
-  const int cap = row_off[b + 1] - r0;
+  const int r1 = row_off[b + 1];
   const int n = n_arr[b];
+  asm volatile("" ::"s"(r0), "s"(r1), "s"(n), "s"(parent), "s"(token), "s"(topk_id), "s"(k));  // and the arguments
+  __builtin_amdgcn_sched_barrier(0);
+  const int cap = r1 - r0;
+  // lanes within the request's row capacity read its rows (padding rows
+  // included: they belong to the request); the rest read nothing
+  const bool in_cap = lane < cap;
+  const int par_ld = in_cap ? parent[r0 + lane] : -1;
+  const int tok_ld = in_cap ? token[r0 + lane] : -1;
+  const int am_ld = in_cap ? topk_id[static_cast<size_t>(r0 + lane) * k] : -1;
+  asm volatile("" ::"v"(par_ld), "v"(tok_ld), "v"(am_ld));
+  __builtin_amdgcn_sched_barrier(0);
   int32_t *path = acc_path + static_cast<size_t>(b) * GRAFT_MAX_NODES;
 
   if (n < 1 || n > cap || n > GRAFT_MAX_NODES) {
@@ -51,7 +65,7 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t *__restrict__ 
   }
 
   const bool valid = lane < n;
-  const int par = valid ? parent[r0 + lane] : -1;
+  const int par = valid ? par_ld : -1;
   const bool pok = !valid || (lane == 0 ? par == -1 : (par >= 0 && par < lane));
   const unsigned long long badmask = __ballot(!pok);
   if (badmask) {
@@ -64,8 +78,8 @@ __global__ __launch_bounds__(64) void accept_kernel(const int32_t *__restrict__ 
     return;
   }
 
-  const int am = valid ? topk_id[static_cast<size_t>(r0 + lane) * k] : -1;  // argmax of this node
-  const int tok = valid ? token[r0 + lane] : -1;
+  const int am = valid ? am_ld : -1;  // argmax of this node
+  const int tok = valid ? tok_ld : -1;
   // edge test: my token against my parent's argmax
   const int parent_am = __shfl(am, par >= 0 ? par : lane);
   int ok = (lane == 0) ? 1 : (valid && tok == parent_am ? 1 : 0);

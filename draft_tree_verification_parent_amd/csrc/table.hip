@@ -112,22 +112,24 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
   __shared__ int s_straddle;  // a request's template rows span two wavefronts
   const int tid = threadIdx.x;
   const int n_elem = upd_rows * k;
+  // Every argument in registers before the first load: fetched lazily, each
+  // would cost a round trip of its own between the loads below.
+  asm volatile("" ::"s"(table), "s"(upd_n), "s"(upd_row_off), "s"(upd_token), "s"(upd_topk), "s"(root_token),
+               "s"(tparent), "s"(trank), "s"(toff), "s"(ret_token), "s"(err), "s"(V), "s"(k), "s"(B_upd),
+               "s"(upd_rows), "s"(B), "s"(tmpl_rows));
 
-  // ---- one round of coalesced loads: offsets, roots, the update list entry
-  // by entry, update tokens, template structure
-  for (int h = tid; h < kSlots; h += kThreads) {
-    s_key[h] = -1;
-    s_val[h] = -1;
-  }
-  for (int b = tid; b <= B; b += kThreads) {
-    s_toff[b] = toff[b];
-    if (b < B) s_root[b] = root_token[b];
-  }
-  for (int b = tid; b <= B_upd; b += kThreads) {
-    s_uoff[b] = upd_row_off[b];
-    if (b < B_upd) s_un[b] = upd_n[b];
-  }
-  if (tid == 0) s_straddle = tmpl_rows > kThreads ? 1 : 0;
+  // ---- one round of coalesced loads into registers: offsets, roots, the
+  // update list entry by entry, update tokens, template structure; only
+  // then the LDS stores (a store between two loads makes the second wait
+  // for the first).  B, B_upd <= kThreads: index kThreads of an offset array
+  // (B + 1 entries) goes to thread 0.
+  static_assert(GRAFT_MAX_BATCH <= kThreads, "one request per thread, plus the last offset");
+  const int toff_a = tid <= B ? toff[tid] : 0;
+  const int root_a = tid < B ? root_token[tid] : 0;
+  const int uoff_a = tid <= B_upd ? upd_row_off[tid] : 0;
+  const int un_a = tid < B_upd ? upd_n[tid] : 0;
+  const int toff_b = tid == 0 && B == kThreads ? toff[kThreads] : 0;
+  const int uoff_b = tid == 0 && B_upd == kThreads ? upd_row_off[kThreads] : 0;
   int ev[kElemRegs];
 #pragma unroll
   for (int q = 0; q < kElemRegs; ++q) {
@@ -139,7 +141,6 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
   for (int u = 0; u < kUpdPer; ++u) {
     const int r = u * kThreads + tid;
     utok[u] = r < upd_rows ? upd_token[r] : -1;
-    if (r < upd_rows) s_rowbad[r] = 0;
   }
   int tpar[kTmplPer], trk[kTmplPer];
 #pragma unroll
@@ -147,6 +148,23 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
     const int t = i * kThreads + tid;
     tpar[i] = t < tmpl_rows ? tparent[t] : -1;
     trk[i] = t < tmpl_rows ? trank[t] : -1;
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of the stores below
+  for (int h = tid; h < kSlots; h += kThreads) {
+    s_key[h] = -1;
+    s_val[h] = -1;
+  }
+  if (tid <= B) s_toff[tid] = toff_a;
+  if (tid < B) s_root[tid] = root_a;
+  if (tid <= B_upd) s_uoff[tid] = uoff_a;
+  if (tid < B_upd) s_un[tid] = un_a;
+  if (tid == 0 && B == kThreads) s_toff[kThreads] = toff_b;
+  if (tid == 0 && B_upd == kThreads) s_uoff[kThreads] = uoff_b;
+  if (tid == 0) s_straddle = tmpl_rows > kThreads ? 1 : 0;
+#pragma unroll
+  for (int u = 0; u < kUpdPer; ++u) {
+    const int r = u * kThreads + tid;
+    if (r < upd_rows) s_rowbad[r] = 0;
   }
   __syncthreads();
 
