@@ -565,7 +565,7 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int max_n) {
   long long want = units > 0 ? (target + units - 1) / units : 1;
   if (want < 1) want = 1;
   long long len = (L + want - 1) / want;
-  len = (len + 31) / 32 * 32;
+  len = (len + KCH - 1) / KCH * KCH;  // whole chunks: a partial last chunk costs a whole one
   if (len < MIN_SPLIT) len = MIN_SPLIT;
   p.split_len = static_cast<int>(len);
   p.nsplit = static_cast<int>((L + len - 1) / len);
