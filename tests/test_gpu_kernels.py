@@ -530,6 +530,39 @@ def test_table_update_conflicts_and_retrieval(api, rows):
     assert got_r.tolist() == exp_r
 
 
+def test_table_largest_batch_1024_requests(api):
+    """1024 update requests and 1024 template requests, the largest batch:
+    the last entry of each offset array is index 1024, one past the
+    workgroup's 1024 threads."""
+    r = np.random.default_rng(1024)
+    V, k = 700, 8
+    table = np.stack([r.choice(V, k, replace=False) for _ in range(V)]).astype(np.int32)
+    B = 1024
+    cap = r.integers(1, 4, B)  # 1..3 update rows per request
+    row_off = np.concatenate([[0], np.cumsum(cap)]).astype(np.int32)
+    rows = int(row_off[-1])
+    n = np.array([int(r.integers(0, c + 1)) for c in cap], np.int32)
+    token = r.integers(0, 60, rows).astype(np.int32)  # same-token conflicts across requests
+    topk = np.stack([r.choice(V, k, replace=False) for _ in range(rows)]).astype(np.int32)
+    roots = r.integers(0, V, B).astype(np.int32)
+    roots[-1] = token[row_off[-2]]  # the last request retrieves from a row the last update request may rewrite
+    tps, trs, toff = [], [], [0]
+    for b in range(B):
+        tp, tr, _ = otemplate(int(r.integers(0, 4)), k, 8)
+        tps += list(tp)
+        trs += list(tr)
+        toff.append(toff[-1] + len(tp))
+    got_t, got_r, err = _table_gpu(api, table, n, row_off, token, topk, roots,
+                                   np.array(tps, np.int32), np.array(trs, np.int32), np.array(toff, np.int32))
+    assert err == 0
+    exp_t = OTab.update(table, n, row_off, token, topk)
+    assert np.array_equal(got_t, exp_t)
+    exp_r = []
+    for b in range(B):
+        exp_r += OTab.retrieve(exp_t, int(roots[b]), tps[toff[b]:toff[b + 1]], trs[toff[b]:toff[b + 1]])
+    assert got_r.tolist() == exp_r
+
+
 def test_table_invalid_rows_are_flagged_and_skipped(api):
     V, k = 50, 4
     table = np.tile(np.arange(k, dtype=np.int32), (V, 1))
