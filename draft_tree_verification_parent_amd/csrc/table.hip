@@ -123,13 +123,16 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
   // then the LDS stores (a store between two loads makes the second wait
   // for the first).  B, B_upd <= kThreads: index kThreads of an offset array
   // (B + 1 entries) goes to thread 0.
+  // The arrays of an empty part may be NULL (nothing reads them then):
+  // their per-request entries count as zero.
   static_assert(GRAFT_MAX_BATCH <= kThreads, "one request per thread, plus the last offset");
-  const int toff_a = tid <= B ? toff[tid] : 0;
-  const int root_a = tid < B ? root_token[tid] : 0;
-  const int uoff_a = tid <= B_upd ? upd_row_off[tid] : 0;
-  const int un_a = tid < B_upd ? upd_n[tid] : 0;
-  const int toff_b = tid == 0 && B == kThreads ? toff[kThreads] : 0;
-  const int uoff_b = tid == 0 && B_upd == kThreads ? upd_row_off[kThreads] : 0;
+  const bool have_t = toff && root_token, have_u = upd_row_off && upd_n;
+  const int toff_a = have_t && tid <= B ? toff[tid] : 0;
+  const int root_a = have_t && tid < B ? root_token[tid] : 0;
+  const int uoff_a = have_u && tid <= B_upd ? upd_row_off[tid] : 0;
+  const int un_a = have_u && tid < B_upd ? upd_n[tid] : 0;
+  const int toff_b = have_t && tid == 0 && B == kThreads ? toff[kThreads] : 0;
+  const int uoff_b = have_u && tid == 0 && B_upd == kThreads ? upd_row_off[kThreads] : 0;
   int ev[kElemRegs];
 #pragma unroll
   for (int q = 0; q < kElemRegs; ++q) {

@@ -563,6 +563,34 @@ def test_table_largest_batch_1024_requests(api):
     assert got_r.tolist() == exp_r
 
 
+def test_table_either_part_empty_with_null_arrays(api):
+    """Either part may be empty with its arrays NULL: an update-only call
+    (no template arrays) and a retrieval-only call (no update arrays)."""
+    r = np.random.default_rng(5)
+    V, k = 200, 8
+    table = np.stack([r.choice(V, k, replace=False) for _ in range(V)]).astype(np.int32)
+    token = np.array([3, 9, 3], np.int32)
+    topk = np.stack([r.choice(V, k, replace=False) for _ in range(3)]).astype(np.int32)
+    n, row_off = np.array([3], np.int32), np.array([0, 3], np.int32)
+    t = dev_i32(table)
+    err = err_buf()
+    api.graft_table_update_retrieve(t, dev_i32(n), dev_i32(row_off), 3, dev_i32(token), dev_i32(topk),
+                                    None, None, None, None, 0, None, err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert np.array_equal(t.cpu().numpy(), OTab.update(table, n, row_off, token, topk))
+    tp, tr, _ = otemplate(20, k, 8)
+    t2 = dev_i32(table)
+    ret = torch.full((20,), -9, dtype=torch.int32, device="cuda")
+    api.graft_table_update_retrieve(t2, None, None, 0, None, None, dev_i32(np.array([5], np.int32)),
+                                    dev_i32(np.array(tp, np.int32)), dev_i32(np.array(tr, np.int32)),
+                                    dev_i32(np.array([0, 20], np.int32)), 20, ret, err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert np.array_equal(t2.cpu().numpy(), table)
+    assert ret.cpu().numpy().tolist() == OTab.retrieve(table, 5, tp, tr)
+
+
 def test_table_invalid_rows_are_flagged_and_skipped(api):
     V, k = 50, 4
     table = np.tile(np.arange(k, dtype=np.int32), (V, 1))
