@@ -19,8 +19,9 @@ SIGNATURES = {
     "graft_version": (c_int, []),
     "graft_table_update_retrieve": (c_int, [P, c_int, c_int, c_int, P, P, c_int, P, P,
                                             c_int, P, P, P, P, c_int, P, P, P]),
-    "graft_build_tree": (c_int, [c_int, c_int, P, P, P, P, c_int, P, P, P, P, P, c_int, c_int,
+    "graft_build_tree": (c_int, [c_int, c_int, P, P, P, P, c_int, P, P, P, P, P, P, c_int, c_int,
                                  c_float, P, P, P, P, P, P, P, P, P, P, P]),
+    "graft_prune_anchor": (c_int, [c_int, P, P, P, P, c_int, P, P, P, P, P, P]),
     "graft_tree_attention_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "graft_tree_attention": (c_int, [c_int, c_int, c_int, c_int, c_float, P, P, P, P, c_int64,
                                      P, c_int, P, c_int, P, P, P, P, P, c_size_t, P, P]),

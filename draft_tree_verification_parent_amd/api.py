@@ -55,17 +55,29 @@ def graft_table_update_retrieve(table, upd_n, upd_row_off, upd_rows, upd_token, 
 
 def graft_build_tree(mode, cand_parent, cand_token, cand_score, cand_off, max_cand, budget,
                      ret_token, ret_parent, ret_off, table, V, k, replace_thresh, ctx_len, row_off,
-                     n_out, parent, token, depth, pos, mask, src, err=None, stream=None):
+                     n_out, parent, token, depth, pos, mask, src, err=None, stream=None, ret_anchor=None):
     B = budget.numel()
     return call("graft_build_tree", B, int(mode), _p(cand_parent, "i32", "cand_parent"),
                 _p(cand_token, "i32", "cand_token"), _p(cand_score, "f32", "cand_score"),
                 _p(cand_off, "i32", "cand_off"), int(max_cand), _p(budget, "i32", "budget"),
                 _p(ret_token, "i32", "ret_token"), _p(ret_parent, "i32", "ret_parent"),
-                _p(ret_off, "i32", "ret_off"), _p(table, "i32", "table"), int(V), int(k),
+                _p(ret_off, "i32", "ret_off"), _p(ret_anchor, "i32", "ret_anchor"),
+                _p(table, "i32", "table"), int(V), int(k),
                 float(replace_thresh), _p(ctx_len, "i32", "ctx_len"), _p(row_off, "i32", "row_off"),
                 _p(n_out, "i32", "n_out"), _p(parent, "i32", "parent"), _p(token, "i32", "token"),
                 _p(depth, "i32", "depth"), _p(pos, "i32", "pos"), _p(mask, "u64", "mask"),
                 _p(src, "i8", "src"), _p(err, "i32", "err"), _s(stream))
+
+
+def graft_prune_anchor(cand_parent, cand_token, cand_score, cand_off, max_cand, budget, stage, anchor,
+                       anchor_token, err=None, stream=None):
+    """Per request: the candidate a tree pruned at checkpoint depth stage[b]
+    hangs its retrieved nodes under, and that candidate's token."""
+    B = budget.numel()
+    return call("graft_prune_anchor", B, _p(cand_parent, "i32", "cand_parent"), _p(cand_token, "i32", "cand_token"),
+                _p(cand_score, "f32", "cand_score"), _p(cand_off, "i32", "cand_off"), int(max_cand),
+                _p(budget, "i32", "budget"), _p(stage, "i32", "stage"), _p(anchor, "i32", "anchor"),
+                _p(anchor_token, "i32", "anchor_token"), _p(err, "i32", "err"), _s(stream))
 
 
 def graft_tree_attention_workspace_bytes(B, Hq, Hkv, d, max_ctx, max_n):

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     const float *__restrict__ cand_score, const int32_t *__restrict__ cand_off, int max_cand,
     const int32_t *__restrict__ budget, const int32_t *__restrict__ ret_token,
     const int32_t *__restrict__ ret_parent, const int32_t *__restrict__ ret_off,
-    const int32_t *__restrict__ table, int V, int k, float thresh,
+    const int32_t *__restrict__ ret_anchor, const int32_t *__restrict__ table, int V, int k, float thresh,
     const int32_t *__restrict__ ctx_len, const int32_t *__restrict__ row_off,
     int32_t *__restrict__ n_out, int32_t *__restrict__ o_parent, int32_t *__restrict__ o_token,
     int32_t *__restrict__ o_depth, int32_t *__restrict__ o_pos, uint64_t *__restrict__ o_mask,
@@ -193,6 +193,8 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
   const int ro = R > 0 ? ret_off[b] : 0;
   const int bud = budget[b];
   const int ctx = ctx_len[b];
+  // candidate under which retrieved nodes with template parent -1 hang
+  const int anc_c = (mode == GRAFT_TREE_PRUNE && ret_anchor) ? ret_anchor[b] : 0;
 
   if (C < 1 || C > max_cand || bud < 1 || R < 0) {
     if (tid == 0) {
@@ -319,9 +321,18 @@ __global__ __launch_bounds__(kThreads) void build_tree_kernel(
     s_nsrc[i] = c == 0 ? GRAFT_SRC_ROOT : GRAFT_SRC_DRAFT;
     s_low[i] = (c > 0 && s_score[c] < thresh) ? 1 : 0;
   }
+  // the anchor must be a kept candidate (the root always is)
+  int anc_i = 0;
+  if (anc_c != 0) {
+    anc_i = (anc_c > 0 && anc_c < C) ? s_idx[anc_c] : -1;
+    if (anc_i < 0) {
+      if (tid == 0) graft::raise_flag(err, GRAFT_ERR_NOT_CLOSED);
+      anc_i = 0;
+    }
+  }
   for (int r = tid; r < Rk; r += kThreads) {
     int tp = s_rpar[r];
-    int p = tp < 0 ? (tail ? nd - 1 : 0) : nd + tp;  // tail: under the deepest kept node
+    int p = tp < 0 ? (tail ? nd - 1 : anc_i) : nd + tp;  // tail: under the deepest kept node
     if (tp >= r) {
       graft::raise_flag(err, GRAFT_ERR_PARENT);
       p = 0;
@@ -416,6 +427,128 @@ __host__ __device__ inline int treegraft_count(int D, int W, int m, int mid_mask
     if (n > max_nodes) return -1;
   }
   return n;
+}
+
+// Retrieval anchor of a tree pruned at checkpoint depth c (Graft page,
+// section 2, second step: the retrieval tree grows from the token generated
+// up to the checkpoint).  The current best path at depth c ends at the best
+// candidate of that depth (c capped at the deepest candidate depth); the
+// anchor is that candidate if the budget keeps it, else its deepest kept
+// ancestor.  One 512-thread workgroup per request: the kept threshold comes
+// from the same workgroup top-64 as the tree build, candidate depths from
+// eleven rounds of pointer jumping in LDS (chains of up to 2048 nodes), the
+// best candidate of depth c from an LDS maximum of the unique keys, and one
+// thread walks up its path to the first kept node (kept keys are exactly
+// those >= the threshold, and a kept node's ancestors are kept).
+__global__ __launch_bounds__(kThreads) void prune_anchor_kernel(
+    const int32_t *__restrict__ cand_parent, const int32_t *__restrict__ cand_token,
+    const float *__restrict__ cand_score, const int32_t *__restrict__ cand_off, int max_cand,
+    const int32_t *__restrict__ budget, const int32_t *__restrict__ stage, int32_t *__restrict__ anchor,
+    int32_t *__restrict__ anchor_token, int32_t *__restrict__ err) {
+  __shared__ int s_par[GRAFT_MAX_CAND];
+  __shared__ float s_sc[GRAFT_MAX_CAND];
+  __shared__ int s_anc[2][GRAFT_MAX_CAND];
+  __shared__ int s_dep[2][GRAFT_MAX_CAND];
+  __shared__ uint64_t s_m1[4][64], s_m2[2][64], s_m3[64];
+  __shared__ uint64_t s_thr, s_best;
+  __shared__ int s_maxdep;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane64 = tid & 63;
+  const int c0 = cand_off[b];
+  const int C = cand_off[b + 1] - c0;
+  const int bud = budget[b];
+  const int depth_c = stage[b];
+  if (C < 1 || C > max_cand || bud < 1) {
+    if (tid == 0) {
+      graft::raise_flag(err, GRAFT_ERR_CAPACITY);
+      anchor[b] = 0;
+      anchor_token[b] = C >= 1 ? cand_token[c0] : -1;
+    }
+    return;
+  }
+  uint64_t kreg[kPasses];
+  bool bad = false;
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int c = pass * kThreads + tid;
+    uint64_t key = 0;
+    if (c < C) {
+      const float sc = cand_score[c0 + c];
+      const int p = cand_parent[c0 + c];
+      const bool pok = c == 0 ? p == -1 : (p >= 0 && p < c);
+      bad |= !pok;
+      s_sc[c] = sc;
+      s_par[c] = pok ? p : (c == 0 ? -1 : 0);  // a broken link is read as the root's
+      s_anc[0][c] = c == 0 ? -1 : s_par[c];
+      s_dep[0][c] = c == 0 ? 0 : 1;
+      if (c > 0)
+        key = (1ull << 43) | (static_cast<uint64_t>(graft::float_order(sc)) << 11) |
+              static_cast<uint64_t>(2047 - c);
+    }
+    kreg[pass] = key;
+  }
+  if (bad) graft::raise_flag(err, GRAFT_ERR_PARENT);
+  if (tid == 0) {
+    s_maxdep = 0;
+    s_best = 0;
+  }
+  const uint64_t top = workgroup_top64(kreg, (C + 63) / 64, wave, lane64, s_m1, s_m2, s_m3);
+  const int need = bud - 1;
+  if (wave == 0) {
+    const int at = need <= 0 ? 0 : (need < 64 ? need - 1 : 63);
+    if (lane64 == at) s_thr = need <= 0 ? ~0ull : top;
+  }
+  // depths: after round j, anc is the 2^j-th ancestor (or -1) and dep the
+  // distance to it (to the root once anc is -1)
+  int cur = 0;
+  for (int round = 0; round < 11; ++round) {
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const int c = pass * kThreads + tid;
+      if (c < C) {
+        const int a = s_anc[cur][c];
+        s_anc[cur ^ 1][c] = a >= 0 ? s_anc[cur][a] : -1;
+        s_dep[cur ^ 1][c] = s_dep[cur][c] + (a >= 0 ? s_dep[cur][a] : 0);
+      }
+    }
+    cur ^= 1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int c = pass * kThreads + tid;
+    if (c < C) atomicMax(&s_maxdep, s_dep[cur][c]);
+  }
+  __syncthreads();
+  const int c_eff = depth_c < s_maxdep ? depth_c : s_maxdep;
+  if (c_eff > 0) {
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass) {
+      const int c = pass * kThreads + tid;
+      if (c >= 1 && c < C && s_dep[cur][c] == c_eff) atomicMax(reinterpret_cast<unsigned long long *>(&s_best),
+                                                               static_cast<unsigned long long>(kreg[pass]));
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int v = 0;
+    if (c_eff > 0 && s_best != 0) {
+      const uint64_t thr = s_thr;
+      v = 2047 - static_cast<int>(s_best & 2047);
+      // climb to the first kept node: key >= thr (the root is always kept)
+      while (v != 0) {
+        const uint64_t key = (1ull << 43) | (static_cast<uint64_t>(graft::float_order(s_sc[v])) << 11) |
+                             static_cast<uint64_t>(2047 - v);
+        if (key >= thr) break;
+        v = s_par[v];
+      }
+    }
+    anchor[b] = v;
+    anchor_token[b] = cand_token[c0 + v];
+  }
 }
 
 // TreeGraft's shared tree (TreeGraft page, section 3: frontier = best W of
@@ -540,7 +673,7 @@ __global__ __launch_bounds__(256) void tail_cut_kernel(int B, int L, const int32
 extern "C" int graft_build_tree(int B, int mode, const int32_t *cand_parent, const int32_t *cand_token,
                                 const float *cand_score, const int32_t *cand_off, int max_cand,
                                 const int32_t *budget, const int32_t *ret_token,
-                                const int32_t *ret_parent, const int32_t *ret_off,
+                                const int32_t *ret_parent, const int32_t *ret_off, const int32_t *ret_anchor,
                                 const int32_t *table, int V, int k, float replace_thresh,
                                 const int32_t *ctx_len, const int32_t *row_off, int32_t *n_out,
                                 int32_t *parent, int32_t *token, int32_t *depth, int32_t *pos,
@@ -563,9 +696,26 @@ extern "C" int graft_build_tree(int B, int mode, const int32_t *cand_parent, con
   graft::clear_error();
   hipLaunchKernelGGL(build_tree_kernel, dim3(B), dim3(kThreads), 0, graft::as_stream(stream), mode,
                      cand_parent, cand_token, cand_score, cand_off, max_cand, budget, ret_token,
-                     ret_parent, ret_off, table, V, k, replace_thresh, ctx_len, row_off, n_out, parent,
+                     ret_parent, ret_off, ret_anchor, table, V, k, replace_thresh, ctx_len, row_off, n_out, parent,
                      token, depth, pos, mask, src, err_flag);
   return graft::check_launch("build_tree");
+}
+
+extern "C" int graft_prune_anchor(int B, const int32_t *cand_parent, const int32_t *cand_token,
+                                  const float *cand_score, const int32_t *cand_off, int max_cand,
+                                  const int32_t *budget, const int32_t *stage, int32_t *anchor,
+                                  int32_t *anchor_token, int32_t *err_flag, graft_stream stream) {
+  using graft::fail;
+  if (B < 0) return fail(GRAFT_EINVAL, "prune_anchor: B=%d", B);
+  if (max_cand < 1 || max_cand > GRAFT_MAX_CAND)
+    return fail(GRAFT_EINVAL, "prune_anchor: max_cand=%d (1..%d)", max_cand, GRAFT_MAX_CAND);
+  if (B == 0) return GRAFT_OK;
+  if (!cand_parent || !cand_token || !cand_score || !cand_off || !budget || !stage || !anchor || !anchor_token)
+    return fail(GRAFT_EINVAL, "prune_anchor: NULL array");
+  graft::clear_error();
+  hipLaunchKernelGGL(prune_anchor_kernel, dim3(B), dim3(kThreads), 0, graft::as_stream(stream), cand_parent,
+                     cand_token, cand_score, cand_off, max_cand, budget, stage, anchor, anchor_token, err_flag);
+  return graft::check_launch("prune_anchor");
 }
 
 extern "C" int graft_tail_cut(int B, int L, const int32_t *root_token, const int32_t *block_token,

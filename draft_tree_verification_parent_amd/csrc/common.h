@@ -33,10 +33,13 @@ __device__ inline bool better(float va, int ia, float vb, int ib) {
 }
 
 // Order-preserving 32-bit image of a float (larger float -> larger integer);
-// -0 is first folded into +0 so that the two compare equal.
+// -0 is first folded into +0 so that the two compare equal.  Every NaN maps
+// to 0, below -inf (0x007FFFFF), so a NaN ranks after every number and NaNs
+// tie with each other (ties go to the lower id).
 __device__ inline uint32_t float_order(float x) {
   const uint32_t u = __float_as_uint(x + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return x == x ? o : 0u;
 }
 
 }  // namespace graft

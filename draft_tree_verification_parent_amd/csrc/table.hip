@@ -198,12 +198,14 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
     if (t < tmpl_rows) {
       town[i] = owner(s_toff, B, t);
       tbase[i] = s_toff[town[i]];
-      const bool link_ok = tpar[i] < t - tbase[i];
-      if (!link_ok) graft::raise_flag(err, GRAFT_ERR_PARENT);
+      // rows before tmpl_off[0] belong to no request: skipped, not flagged
+      const bool in_req = t >= tbase[i];
+      const bool link_ok = in_req & (tpar[i] < t - tbase[i]);
+      if (in_req & !link_ok) graft::raise_flag(err, GRAFT_ERR_PARENT);
       s_round[t] = link_ok ? -1 : 0;
       s_bad[t] = link_ok ? 0 : 1;
       if (link_ok) pend |= 1u << i;
-      if ((tbase[i] >> 6) != (t >> 6)) s_straddle = 1;
+      if (in_req & ((tbase[i] >> 6) != (t >> 6))) s_straddle = 1;
     }
   }
   __syncthreads();
@@ -215,7 +217,8 @@ __global__ __launch_bounds__(kThreads) void update_retrieve_kernel(
     const int r = u * kThreads + tid;
     if (r < upd_rows) {
       const int b = owner(s_uoff, B_upd, r);
-      const bool live = r - s_uoff[b] < s_un[b] && r < s_uoff[b + 1];  // not a padding row
+      // a node of request b (not a padding row, not a row before upd_row_off[0])
+      const bool live = (r >= s_uoff[b]) & (r - s_uoff[b] < s_un[b]) & (r < s_uoff[b + 1]);
       int t = -1;
       if (live) {
         if (utok[u] >= 0 && utok[u] < V && !s_rowbad[r]) t = utok[u];

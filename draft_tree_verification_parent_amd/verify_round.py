@@ -2,9 +2,11 @@
 
 Order on one HIP stream (Graft page, arXiv:2605.20104 write-up, section 2;
 section 6, second level):
+  0. graft_prune_anchor          -- (trees pruned past checkpoint 0) the
+                                    retrieval anchor inside the draft tree;
   1. graft_table_update_retrieve -- the previous round's verified positions
      rewrite their table rows, then the retrieval template is expanded from
-     the current root token;
+     the current root token (or the anchor's);
   2. graft_build_tree            -- select, append retrieved nodes, flatten,
                                     depth / positions / mask;
   3. graft_tree_attention        -- one tree-masked attention layer;
@@ -64,7 +66,12 @@ class VerifyRound:
         else:
             base = STEPS_FUSED if fused else STEPS_SPLIT
         self.tail = bool(getattr(ri.wl, "tail", False))
+        stage = getattr(ri, "stage", None)
+        # trees pruned past checkpoint 0 retrieve from an anchor inside the draft tree
+        self.anchored = stage is not None and bool(np.any(np.asarray(stage) > 0))
         pre = ("tail_cut",) if self.tail else (("treegraft",) if getattr(ri, "tg_tok", None) is not None else ())
+        if self.anchored:
+            pre = pre + ("prune_anchor",)
         self.steps = pre + base + (("kv_compact",) if chain else ())
         wl = ri.wl
         self.ri, self.wl, self.dev = ri, wl, dev
@@ -108,6 +115,10 @@ class VerifyRound:
         self.cand_off = _i32(cand_off, dev)
         self.max_cand = int(np.max(np.diff(cand_off)))
         self.budget = _i32(ri.budget, dev)
+        if self.anchored:
+            self.stage = _i32(stage, dev)
+            self.anchor = torch.empty(B, dtype=torch.int32, device=dev)
+            self.anchor_token = torch.empty(B, dtype=torch.int32, device=dev)
         self.ctx_len = _i32(ri.ctx_len, dev)
         # chained rounds plan attention for the largest context the cache
         # can still hold a tree after
@@ -213,9 +224,14 @@ class VerifyRound:
         api.graft_tail_cut(self.root_token, self.block_token, self.block_conf, self.wl.replace_thresh,
                            self.tail_keep, self.tail_root)
 
+    def step_prune_anchor(self):
+        api.graft_prune_anchor(self.cand_parent, self.cand_token, self.cand_score, self.cand_off, self.max_cand,
+                               self.budget, self.stage, self.anchor, self.anchor_token, self.err)
+
     def step_update_retrieve(self):
         u = self.upd
-        root = self.tail_root if self.tail else self.root_token  # Graft-TAIL: the deepest kept node
+        # Graft-TAIL: the deepest kept node; checkpoint pruning: the anchor
+        root = self.tail_root if self.tail else (self.anchor_token if self.anchored else self.root_token)
         api.graft_table_update_retrieve(self.table, u["n"], u["row_off"], u["rows"], u["token"],
                                         u["topk"], root, self.tmpl_parent, self.tmpl_rank,
                                         self.tmpl_off, self.tmpl_rows, self.ret_token, self.err)
@@ -226,7 +242,8 @@ class VerifyRound:
                              self.tmpl_parent, self.tmpl_off if self.tmpl_rows else None,
                              self.table, self.V, self.k, self.wl.replace_thresh, self.ctx_len,
                              self.row_off, self.n_out, self.parent, self.token, self.depth,
-                             self.pos, self.mask, self.src, self.err)
+                             self.pos, self.mask, self.src, self.err,
+                             ret_anchor=self.anchor if self.anchored else None)
 
     def step_tree_attention(self):
         wl = self.wl

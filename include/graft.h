@@ -9,6 +9,9 @@
  *                                token's retrieval template is expanded
  *   graft_build_tree             draft selection + retrieved nodes, flatten,
  *                                depth / positions / ancestor mask
+ *   graft_prune_anchor           (trees pruned at a checkpoint) the node the
+ *                                retrieved nodes hang under, and its token,
+ *                                the retrieval root
  *   graft_tree_attention         tree-masked GQA attention over the KV cache
  *   graft_lmhead_topk            logits = hidden . W^T and per-row top-k
  *                                (weights packed once by graft_lmhead_pack)
@@ -51,6 +54,8 @@
  *    misaligned pointer or stride returns GRAFT_EINVAL; a misaligned kv_off
  *    entry (device data) raises GRAFT_ERR_ALIGN and skips that request.
  *  - Integer results are exact; ties in any ranking go to the lower index.
+ *    A NaN score or logit ranks below every number (NaNs tie with each
+ *    other); -0 and +0 tie.
  *  - bf16 tensors are raw bfloat16 bit patterns (uint16).
  */
 #ifndef GRAFT_H
@@ -119,7 +124,8 @@ int graft_version(void);
  *   upd_topk [rows, k] (device, row-major, the top-k ids of each row).  For
  *   node r the whole row table[upd_token[r]] becomes upd_topk[r]; when
  *   several nodes carry the same token the largest row index wins.
- *   upd_rows (host) = upd_row_off[B_upd] <= GRAFT_MAX_UPDATE_ROWS.
+ *   upd_rows (host) = upd_row_off[B_upd] <= GRAFT_MAX_UPDATE_ROWS; rows
+ *   before upd_row_off[0] belong to no request and are ignored.
  *   A node whose token or ids fall outside [0, V) is skipped (ERR_TOKEN).
  * Retrieval (after the update): request b's template nodes are
  *   tmpl_off[b] .. tmpl_off[b+1]-1 (device) with request-local template
@@ -128,7 +134,8 @@ int graft_version(void);
  *     ret_token[t] = table'[token of its parent (root_token[b] for -1)][rank]
  *   where table' is the updated table.  tmpl_rows (host) = tmpl_off[B] <=
  *   GRAFT_MAX_TEMPLATE_ROWS.  Invalid links yield ret_token = -1 with
- *   ERR_PARENT / ERR_RANK / ERR_TOKEN.
+ *   ERR_PARENT / ERR_RANK / ERR_TOKEN.  Rows before tmpl_off[0] belong to
+ *   no request: ret_token = -1, nothing flagged.
  * Either part may be empty (B_upd = 0 or upd_rows = 0; B = 0 or
  * tmpl_rows = 0).  B, B_upd <= GRAFT_MAX_BATCH (their offsets are staged in
  * LDS); larger batches return GRAFT_EINVAL.  One workgroup; calls that
@@ -157,8 +164,12 @@ int graft_table_update_retrieve(int32_t *table, int V, int k,
  * budget[b] (device): draft nodes kept, root included: the root plus the
  *   budget-1 best other candidates by (score desc, index asc).
  * mode GRAFT_TREE_PRUNE: the request's retrieved nodes ret_off[b] ..
- *   ret_off[b+1]-1 (ret_token, ret_parent = template parents, -1 = root)
- *   are appended after the kept draft nodes.  ret_* may be NULL for none.
+ *   ret_off[b+1]-1 (ret_token, ret_parent = template parents, -1 = the
+ *   anchor) are appended after the kept draft nodes.  ret_* may be NULL
+ *   for none.  ret_anchor (device int32 [B], may be NULL = every request's
+ *   root): the candidate the retrieved nodes hang under, e.g. from
+ *   graft_prune_anchor; one that is not kept flags ERR_NOT_CLOSED and the
+ *   root is used.
  * mode GRAFT_TREE_STATIC_REPLACE: no retrieved nodes; a kept draft node
  *   with score < replace_thresh that is the j-th (0-based, by index) such
  *   child of its parent takes token table[token(parent)][j] when j < k
@@ -187,11 +198,32 @@ int graft_build_tree(int B, int mode,
                      const int32_t *cand_parent, const int32_t *cand_token, const float *cand_score,
                      const int32_t *cand_off, int max_cand, const int32_t *budget,
                      const int32_t *ret_token, const int32_t *ret_parent, const int32_t *ret_off,
-                     const int32_t *table, int V, int k, float replace_thresh,
+                     const int32_t *ret_anchor, const int32_t *table, int V, int k, float replace_thresh,
                      const int32_t *ctx_len, const int32_t *row_off,
                      int32_t *n_out, int32_t *parent, int32_t *token, int32_t *depth,
                      int32_t *pos, uint64_t *mask, int8_t *src, int32_t *err_flag,
                      graft_stream stream);
+
+/*
+ * Retrieval anchor of trees pruned at a checkpoint (Graft page, section 2,
+ * second step: the drafter's tree is checked at depths 0, 1 and 5 by the
+ * current best path's cumulative confidence; when pruning triggers, the
+ * retrieval tree is expanded from the token generated up to that point).
+ * This library's reading: the best path at checkpoint depth c ends at the
+ * candidate of depth c with the highest cumulative score (ties: lower
+ * index; c is capped at the deepest candidate depth); the anchor is that
+ * candidate when graft_build_tree's budget keeps it, else its deepest kept
+ * ancestor.  c <= 0 anchors at the root.
+ * Candidates, max_cand and budget (device) as in graft_build_tree;
+ * stage (device int32 [B]) = each request's checkpoint depth c.
+ * Outputs (device int32 [B]): anchor[b] = the request-local candidate index
+ * (pass as graft_build_tree's ret_anchor) and anchor_token[b] = its token
+ * (pass as graft_table_update_retrieve's root_token).  A malformed candidate
+ * list flags ERR_CAPACITY / ERR_PARENT and anchors at the root.
+ */
+int graft_prune_anchor(int B, const int32_t *cand_parent, const int32_t *cand_token, const float *cand_score,
+                       const int32_t *cand_off, int max_cand, const int32_t *budget, const int32_t *stage,
+                       int32_t *anchor, int32_t *anchor_token, int32_t *err_flag, graft_stream stream);
 
 /*
  * TreeGraft's shared draft tree from a small and a mid drafter (TreeGraft

@@ -38,10 +38,21 @@ def tree_stage(ri, dmax: int = 8):
     cand_parent, cand_token, cand_score, cand_off = ri.cand_parent, ri.cand_token, ri.cand_score, ri.cand_off
     if getattr(ri, "tg_tok", None) is not None:
         cand_parent, cand_token, cand_score, cand_off = treegraft_candidates(ri)
+    # Graft's checkpoints: a tree pruned at checkpoint depth c retrieves from
+    # the deepest kept node of the best path at depth c (the root at c = 0)
+    stage = getattr(ri, "stage", None)
+    anchor = np.zeros(ri.B, np.int32)
+    if stage is not None:
+        for b in range(ri.B):
+            c0, c1 = int(cand_off[b]), int(cand_off[b + 1])
+            if int(stage[b]) > 0:
+                anchor[b] = _tree.retrieval_anchor(cand_parent[c0:c1], cand_score[c0:c1], int(ri.budget[b]),
+                                                   int(stage[b]))
     tp_all, tr_all, rt_all, off = [], [], [], [0]
     for b in range(ri.B):
         tp, tr, _ = _template.template(int(ri.n_ret[b]), ri.k, dmax)
-        rt = _table.retrieve(table, int(ri.root_token[b]), tp, tr)
+        root = int(cand_token[int(cand_off[b]) + int(anchor[b])]) if anchor[b] else int(ri.root_token[b])
+        rt = _table.retrieve(table, root, tp, tr)
         tp_all += tp
         tr_all += tr
         rt_all += rt
@@ -54,9 +65,9 @@ def tree_stage(ri, dmax: int = 8):
     tree = _tree.build_batch(cand_parent, cand_token, cand_score, cand_off,
                              ri.budget, ret_token, tparent, tmpl_off, ri.ctx_len, ri.V,
                              ri.row_off, static_replace=wl.static_replace, table=table,
-                             replace_thresh=wl.replace_thresh)
+                             replace_thresh=wl.replace_thresh, anchor=anchor)
     return dict(table=table, tparent=tparent, trank=trank, tmpl_off=tmpl_off,
-                ret_token=ret_token, tree=tree)
+                ret_token=ret_token, tree=tree, anchor=anchor)
 
 
 def treegraft_candidates(ri):

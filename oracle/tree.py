@@ -8,9 +8,14 @@
   stage budgets keep 8 / 24 / 40 draft nodes of 60 slots (Graft page,
   section 2, second step).  Ties in score go to the lower candidate index.
 * Retrieved nodes are appended after the kept draft nodes, in template
-  order; a template parent of -1 means the tree root (Graft page, section
-  2: the retrieval tree is rooted at the current token and fills the slots
-  pruning freed).
+  order; a template parent of -1 means the retrieval anchor (Graft page,
+  section 2, second step: when pruning triggers at a checkpoint depth, the
+  retrieval tree is expanded from the token generated up to that point and
+  fills the slots pruning freed).  Reading (retrieval_anchor): the current
+  best path at checkpoint depth c ends at the candidate of depth c with the
+  highest cumulative score; the anchor is the deepest kept node on that
+  path (all of it when the budget keeps it).  At checkpoint 0 the anchor is
+  the root.
 * Static replacement (Graft page, section 4, batched-serving paragraph):
   the per-request slot count stays fixed and low-confidence draft nodes are
   swapped for retrieved tokens.  Reading: a node whose score is below the
@@ -39,8 +44,49 @@ def select_draft(score: np.ndarray, budget: int) -> list[int]:
     C = len(score)
     if C < 1 or budget < 1:
         raise OracleError("empty candidate set or budget")
-    rest = sorted(range(1, C), key=lambda c: (-float(score[c]), c))
+    rest = sorted(range(1, C), key=lambda c: score_rank_key(score[c], c))
     return sorted([0] + rest[: budget - 1])
+
+
+def score_rank_key(s, c: int):
+    """Sort key of candidate c with score s: score descending, index
+    ascending; a NaN score ranks below every number (the scores are products
+    of probabilities, so NaN is not a valid score; its place is fixed so that
+    a NaN never displaces a real candidate).  -0 and +0 tie."""
+    s = float(s)
+    return (1, 0.0, c) if s != s else (0, -s, c)
+
+
+def candidate_depths(cand_parent) -> list[int]:
+    """Depth of every candidate (parents precede their children)."""
+    dep = []
+    for c in range(len(cand_parent)):
+        p = int(cand_parent[c])
+        dep.append(0 if c == 0 else dep[p] + 1)
+    return dep
+
+
+def retrieval_anchor(cand_parent, cand_score, budget: int, depth_c: int) -> int:
+    """Candidate under which the retrieved nodes of a tree pruned at
+    checkpoint depth depth_c hang: the best candidate (score descending,
+    index ascending) of depth min(depth_c, deepest candidate depth), or, if
+    the budget does not keep it, its deepest kept ancestor."""
+    C = len(cand_parent)
+    for c in range(1, C):
+        if not (0 <= int(cand_parent[c]) < c):
+            raise OracleError("candidate parent must precede its child")
+    if depth_c < 0:
+        raise OracleError("checkpoint depth must be >= 0")
+    dep = candidate_depths(cand_parent)
+    c_eff = min(depth_c, max(dep))
+    if c_eff == 0:
+        return 0
+    best = min((c for c in range(1, C) if dep[c] == c_eff), key=lambda c: score_rank_key(cand_score[c], c))
+    kept = set(select_draft(cand_score, budget))
+    v = best
+    while v not in kept:
+        v = int(cand_parent[v])
+    return v
 
 
 def ancestors_or_self(parent: list[int], i: int) -> list[int]:
@@ -54,10 +100,11 @@ def ancestors_or_self(parent: list[int], i: int) -> list[int]:
 
 def build_one(cand_parent, cand_token, cand_score, budget, ret_token, ret_parent,
               ctx_len: int, V: int, static_replace: bool = False, table=None,
-              replace_thresh: float = 0.0):
-    """One request.  Returns dict of python lists: parent, token, depth, pos,
-    mask (python int), src, score (draft score or None), cand (candidate
-    index or -1)."""
+              replace_thresh: float = 0.0, anchor: int = 0):
+    """One request.  Retrieved nodes with template parent -1 hang under
+    candidate `anchor` (0 = the root), which must be kept.  Returns dict of
+    python lists: parent, token, depth, pos, mask (python int), src, score
+    (draft score or None), cand (candidate index or -1)."""
     C = len(cand_parent)
     if C < 1 or int(cand_parent[0]) != -1:
         raise OracleError("candidate 0 must be the root")
@@ -84,6 +131,8 @@ def build_one(cand_parent, cand_token, cand_score, budget, ret_token, ret_parent
         score.append(float(cand_score[c]))
         cand.append(c)
     nd = len(kept)
+    if anchor not in newidx:
+        raise OracleError("the retrieval anchor is not a kept candidate")
     R = len(ret_token)
     for r in range(R):
         tp = int(ret_parent[r])
@@ -91,7 +140,7 @@ def build_one(cand_parent, cand_token, cand_score, budget, ret_token, ret_parent
             raise OracleError("template parent must precede its child")
         if not (0 <= int(ret_token[r]) < V):
             raise OracleError("retrieved token outside the vocabulary")
-        parent.append(0 if tp < 0 else nd + tp)
+        parent.append(newidx[anchor] if tp < 0 else nd + tp)
         token.append(int(ret_token[r]))
         src.append(SRC_RETRIEVED)
         score.append(None)
@@ -131,10 +180,11 @@ def build_one(cand_parent, cand_token, cand_score, budget, ret_token, ret_parent
 
 def build_batch(cand_parent, cand_token, cand_score, cand_off, budget,
                 ret_token, ret_parent, ret_off, ctx_len, V, row_off,
-                static_replace=False, table=None, replace_thresh=0.0):
+                static_replace=False, table=None, replace_thresh=0.0, anchor=None):
     """All requests, written in the padded row layout: request b's node i
     sits at row row_off[b] + i.  Rows past n[b] hold parent=token=depth=
-    pos=-1, mask=0, src=-1."""
+    pos=-1, mask=0, src=-1.  anchor[b]: request b's retrieval anchor
+    (candidate index; None = every request's root)."""
     B = len(budget)
     rows = int(row_off[B])
     out = dict(parent=np.full(rows, -1, np.int32), token=np.full(rows, -1, np.int32),
@@ -147,7 +197,8 @@ def build_batch(cand_parent, cand_token, cand_score, cand_off, budget,
         r0, r1 = int(ret_off[b]), int(ret_off[b + 1])
         t = build_one(cand_parent[c0:c1], cand_token[c0:c1], cand_score[c0:c1],
                       int(budget[b]), ret_token[r0:r1], ret_parent[r0:r1],
-                      int(ctx_len[b]), V, static_replace, table, replace_thresh)
+                      int(ctx_len[b]), V, static_replace, table, replace_thresh,
+                      0 if anchor is None else int(anchor[b]))
         cap = int(row_off[b + 1]) - int(row_off[b])
         if t["n"] > cap:
             raise OracleError("tree larger than the request's row capacity")

@@ -33,6 +33,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import OracleError
+from .tree import score_rank_key
 
 
 def node_count(D: int, W: int, m: int, mid_mask: int) -> int:
@@ -69,7 +70,7 @@ def build(root_token: int, D: int, W: int, m: int, mid_mask: int, tok, p, q):
         else:
             pool = [v for v in range(len(parent)) if created[v] == k]
             score = s
-        frontier = sorted(pool, key=lambda v: (-float(score[v]), v))[:W]
+        frontier = sorted(pool, key=lambda v: score_rank_key(score[v], v))[:W]
         if mid:
             for v in pool:
                 visited[v] = True

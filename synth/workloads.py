@@ -59,6 +59,8 @@ class Workload:
     m: int = 10       # children per frontier node
     tail: bool = False  # Graft-TAIL on a block draft of n_nodes - 1 tokens
     mid_mask: int = -1  # >= 0: TreeGraft shared tree built on the device (bit k: step k by the mid drafter)
+    stages: tuple = ()  # per-request pruning checkpoint (0, 1, 5; -1 = none), cycled over the batch; sets
+    #                     the draft budget and retrieved count per request (Graft's 60-slot split)
 
     def with_ctx(self, lo: int, hi: int | None = None) -> "Workload":
         d = dict(self.__dict__)
@@ -84,10 +86,10 @@ WORKLOADS = {
                    "lm-head 4096x151936, table 151936x10",
                 B=1, Hq=32, Hkv=8, d=128, H=4096, V=151936, k=10, ctx_lo=32768, ctx_hi=32768,
                 tree="eagle", n_nodes=63, draft_budget=63, n_retrieved=0),
-    4: Workload(4, "Qwen3-14B-shaped long context: 40q/8kv d128, ctx 65536, 60 slots = 24 draft + 36 retrieved, "
-                   "lm-head 5120x151936, table 151936x8 warmed from a repetitive context",
+    4: Workload(4, "Qwen3-14B-shaped long context: 40q/8kv d128, ctx 65536, 60 slots = 24 draft + 36 retrieved "
+                   "(pruned at checkpoint 1), lm-head 5120x151936, table 151936x8 warmed from a repetitive context",
                 B=1, Hq=40, Hkv=8, d=128, H=5120, V=151936, k=8, ctx_lo=65536, ctx_hi=65536,
-                tree="eagle", n_nodes=60, draft_budget=24, n_retrieved=36, ctx_tokens=True),
+                tree="eagle", n_nodes=60, draft_budget=24, n_retrieved=36, ctx_tokens=True, stages=(1,)),
     5: Workload(5, "batched static tree: 16 requests, Qwen3-8B shapes, ctx U[4096,16384], 60-slot trees with "
                    "score<0.05 nodes replaced from a shared 151936x8 table",
                 B=16, Hq=32, Hkv=8, d=128, H=4096, V=151936, k=8, ctx_lo=4096, ctx_hi=16384,
@@ -101,7 +103,15 @@ WORKLOADS = {
                    "drafter at step 2, pruned to Bver=63, lm-head 4096x151936, table 151936x10",
                 B=1, Hq=32, Hkv=8, d=128, H=4096, V=151936, k=10, ctx_lo=32768, ctx_hi=32768,
                 tree="treegraft", n_nodes=63, draft_budget=63, n_retrieved=0, mid_mask=0b00100),
+    8: Workload(8, "Graft stage-adaptive batch: 4 requests, Qwen3-8B shapes, ctx U[4096,8192], 60 slots pruned at "
+                   "checkpoints 5, 1, 0 and not at all (40+20, 24+36, 8+52, 60+0), table 151936x8",
+                B=4, Hq=32, Hkv=8, d=128, H=4096, V=151936, k=8, ctx_lo=4096, ctx_hi=8192,
+                tree="eagle", n_nodes=60, draft_budget=40, n_retrieved=20, stages=(5, 1, 0, -1)),
 }
+
+# Graft's split of 60 verify slots by pruning checkpoint (Graft page, section
+# 2, second step): checkpoint depth -> (draft nodes with the root, retrieved)
+STAGE_SLOTS = {-1: (60, 0), 0: (8, 52), 1: (24, 36), 5: (40, 20)}
 
 
 # ----------------------------------------------------------------------------
@@ -354,11 +364,16 @@ def make_round_inputs(wl: Workload, kv: bool = True, extra_slots: int = 0) -> Ro
         root_token=np.array(roots, np.int32),
         budget=np.full(B, wl.draft_budget, np.int32),
         n_ret=np.full(B, wl.n_retrieved, np.int32),
+        stage=None,
         row_off=(np.arange(B + 1) * N).astype(np.int32),
         table=table,
         prev_n=prev_n, prev_row_off=prev_row_off, prev_token=prev_token, prev_topk=prev_topk,
         scale=float(1.0 / np.sqrt(wl.d)),
     )
+    if wl.stages:  # per-request checkpoint: budget and retrieved count from Graft's split
+        ri.stage = np.array([wl.stages[b % len(wl.stages)] for b in range(B)], np.int32)
+        ri.budget = np.array([STAGE_SLOTS[int(s)][0] for s in ri.stage], np.int32)
+        ri.n_ret = np.array([STAGE_SLOTS[int(s)][1] for s in ri.stage], np.int32)
     if tg_out:  # TreeGraft: per request tok [D][W][m], prob [D][W][m], q [1 + D*W*m]
         ri.tg_mask = np.full(B, wl.mid_mask, np.int32)
         ri.tg_tok = np.stack([o[0] for o in tg_out])

@@ -91,9 +91,14 @@ def test_host_argument_validation_launches_nothing(native):
     assert L.graft_tree_attention(0, 8, 2, 128, 0.1, *args) == 0
     # build tree
     bt = [1] * 24
-    assert L.graft_build_tree(1, 7, *bt[:4], 10, *bt[:5], 100, 8, 0.0, *bt[:11]) == E
-    assert L.graft_build_tree(1, 0, *bt[:4], 5000, *bt[:5], 100, 8, 0.0, *bt[:11]) == E
-    assert L.graft_build_tree(0, 0, *bt[:4], 10, *bt[:5], 100, 8, 0.0, *bt[:11]) == 0
+    assert L.graft_build_tree(1, 7, *bt[:4], 10, *bt[:6], 100, 8, 0.0, *bt[:11]) == E
+    assert L.graft_build_tree(1, 0, *bt[:4], 5000, *bt[:6], 100, 8, 0.0, *bt[:11]) == E
+    assert L.graft_build_tree(0, 0, *bt[:4], 10, *bt[:6], 100, 8, 0.0, *bt[:11]) == 0
+    # retrieval anchor
+    assert L.graft_prune_anchor(1, *bt[:4], 0, *bt[:5], None, None) == E          # max_cand 0
+    assert L.graft_prune_anchor(1, *bt[:4], 3000, *bt[:5], None, None) == E       # above GRAFT_MAX_CAND
+    assert L.graft_prune_anchor(1, *bt[:4], 10, 1, None, 1, 1, None, None) == E   # NULL stage
+    assert L.graft_prune_anchor(0, *bt[:4], 10, *bt[:5], None, None) == 0
     # table
     assert L.graft_table_update_retrieve(1, 100, 17, 0, None, None, 0, None, None, 0, None, None,
                                          None, None, 0, None, None, None) == E
@@ -200,7 +205,7 @@ def test_tail_host_validation_launches_nothing(native):
     assert L.graft_tail_cut(4, 16, p, p, None, 0.5, p, p, None) == E
     assert L.graft_tail_cut(0, 16, None, None, None, 0.5, None, None, None) == 0
     # build_tree accepts the tail mode (and still rejects unknown ones)
-    args = [p, p, p, p, 17, p, None, None, None, None, 1000, 8, 0.5, p, p, p, p, p, p, p, p, p, None, None]
+    args = [p, p, p, p, 17, p, None, None, None, None, None, 1000, 8, 0.5, p, p, p, p, p, p, p, p, p, None, None]
     assert L.graft_build_tree(0, 2, *args) == 0
     assert L.graft_build_tree(1, 3, *args) == E
 

@@ -105,3 +105,35 @@ def test_topk_special_cases():
     ids, vals = TK.topk(y, 8)
     assert ids[2, 0] == 777 and vals[2, 0] == 100.0
     assert np.all(np.diff(vals, axis=1) <= 0)
+
+
+def test_topk_nan_ranks_below_every_number():
+    """A NaN logit ranks after every number, -inf included; NaNs tie with
+    each other (lower id first).  Checked against the same order written out
+    as repeated extraction of the best remaining entry."""
+    r = np.random.default_rng(7)
+    x = r.integers(-3, 3, (4, 23)).astype(np.float32)
+    x[0, [0, 5, 9]] = np.nan
+    x[1, :] = np.nan
+    x[1, [4, 17]] = [-np.inf, 2.0]
+    x[2, [3, 4]] = [np.inf, np.nan]
+    for m in range(4):
+        remaining = list(range(x.shape[1]))
+        order = []
+        while remaining:
+            def beats(a, b):
+                va, vb = x[m, a], x[m, b]
+                if np.isnan(vb) and not np.isnan(va):
+                    return True
+                if np.isnan(va):
+                    return np.isnan(vb) and a < b
+                return va > vb or (va == vb and a < b)
+            best = remaining[0]
+            for c in remaining[1:]:
+                if beats(c, best):
+                    best = c
+            order.append(best)
+            remaining.remove(best)
+        ids, vals = TK.topk(x[m:m + 1], 12)
+        assert ids[0].tolist() == order[:12]
+        assert np.array_equal(vals[0], x[m, order[:12]], equal_nan=True)

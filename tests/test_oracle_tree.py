@@ -180,3 +180,58 @@ def test_static_replace_properties():
             assert t["token"][i] in set(table[t["token"][t["parent"][i]]].tolist())
         else:
             assert t["token"][i] == base["token"][i]
+
+
+def test_nan_scores_rank_last():
+    """A NaN candidate score ranks below every number (ties among NaNs and
+    between -0 and +0 go to the lower index)."""
+    score = np.array([1.0, np.nan, 0.5, -0.0, np.nan, 0.0, 0.25, 0.5], np.float32)
+    assert T.select_draft(score, 1) == [0]
+    assert T.select_draft(score, 3) == [0, 2, 7]
+    assert T.select_draft(score, 6) == [0, 2, 3, 5, 6, 7]
+    assert T.select_draft(score, 7) == [0, 1, 2, 3, 5, 6, 7]
+    assert T.select_draft(score, 8) == list(range(8))
+
+
+def test_hand_worked_retrieval_anchor():
+    """Retrieval hangs under the deepest kept node of the best path at the
+    checkpoint depth (tests/golden/tree_anchor.json, worked by hand)."""
+    g = _load("tree_anchor.json")
+    cp = np.array(g["cand_parent"])
+    cs = np.array(g["cand_score"], np.float32)
+    for case in g["cases"]:
+        a = T.retrieval_anchor(cp, cs, case["budget"], case["depth_c"])
+        assert a == case["anchor"], case["name"]
+        t = T.build_one(cp, np.array(g["cand_token"]), cs, case["budget"], np.array(case["ret_token"]),
+                        np.array(case["ret_parent"]), g["ctx_len"], g["V"], anchor=a)
+        e = case["expect"]
+        assert t["n"] == e["n"], case["name"]
+        for key in ("parent", "token", "depth", "pos", "mask", "src"):
+            assert list(t[key]) == e[key], (case["name"], key)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_retrieval_anchor_properties(seed):
+    """On the drafter stand-in's candidates: the anchor is kept; it lies on
+    the root path of the best candidate at the checkpoint depth and no
+    deeper node of that path is kept; checkpoint 0 gives the root; at
+    checkpoint 1 the best depth-1 candidate is always kept (every other
+    candidate scores at most as high as its own depth-1 ancestor)."""
+    r = np.random.default_rng(seed)
+    par, tok, sc = W.eagle_candidates(r, 5000, 5, 10, 10, 7)
+    dep = T.candidate_depths(par)
+    for depth_c, budget in ((0, 8), (1, 24), (5, 40), (5, 12), (3, 6), (9, 60)):
+        a = T.retrieval_anchor(par, sc, budget, depth_c)
+        kept = set(T.select_draft(sc, budget))
+        assert a in kept
+        c_eff = min(depth_c, max(dep))
+        if c_eff == 0:
+            assert a == 0
+            continue
+        at_c = [c for c in range(1, len(par)) if dep[c] == c_eff]
+        best = max(at_c, key=lambda c: (float(sc[c]), -c))
+        path = T.ancestors_or_self(list(par), best)
+        assert a in path
+        assert all(v not in kept for v in path[:path.index(a)])
+        if depth_c == 1:
+            assert a == best
