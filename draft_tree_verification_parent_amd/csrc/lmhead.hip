@@ -887,6 +887,277 @@ __global__ __launch_bounds__(256, 1) void lmhead_wide_kernel(int M, int H, int V
   }
 }
 
+
+// ------------------------------------------------ packed W, 256 x 256 tiles
+// Past 128 hidden rows every byte a CU takes in is worth more flops with a
+// bigger tile: a 256 x 256 tile (hidden rows x vocabulary rows) feeds 128
+// flops per byte taken in against the 128 x 256 tile's 85, and the CU's
+// intake rate (30-35 GB/s once HBM misses share its request stream) is what
+// bounds this product.  4 wavefronts, each a 128 x 128 block (2 x 2 layout):
+// 64 accumulator tiles (256 accumulation registers) and 8 + 8 fragments per
+// k-step, read as in the 128-row kernel from 128-byte LDS rows swizzled by
+// (r % 8).
+//
+// A chunk is 64 hidden columns: 32 KB of W (two packed images) and 32 KB of
+// hidden rows.  W goes through a ring of three stages and the hidden rows
+// through a ring of two (160 KB in all), so that, while chunk q is
+// computed, W of chunks q + 1 and q + 2 and the hidden rows of chunk q + 1
+// are in flight: 96 KB, and the memory pipe never drains between chunks.
+// At the top of chunk q the wave waits for W_q and H_q (issued before W_q+1,
+// which may stay in flight); H_q+1 and W_q+2 go into the stages chunk q - 1
+// used, one DMA among each group of 8 MFMAs.
+//
+// Epilogue (per tile): one thread per hidden row keeps one persistent sorted
+// list of k keys.  The tile's logits pass through the chunk's two consumed
+// stages (rows 0-127 in its W stage, 128-255 in its hidden stage) in 8
+// passes of 32 vocabulary columns; each thread screens its row's 32 entries
+// against its own k-th key.  One list per (row, workgroup) is written at the
+// end and merged by topk_merge_kernel.  The MFMA sums run in the k-order of
+// every other path, so the logits are bit-identical.
+constexpr int BG_BM = 256;  // hidden rows per tile
+constexpr int BG_BV = 256;  // vocabulary rows per tile
+
+template <int K>
+__global__ __launch_bounds__(256, 1) void lmhead_big_kernel(int M, int H, int V, int k,
+                                                          const graft_bf16 *__restrict__ hidden,
+                                                          const unsigned char *__restrict__ wpk,
+                                                          uint64_t *__restrict__ part_out, int tiles_m, int tiles_v,
+                                                          int n_img) {
+  constexpr int WB = BG_BV * WD_KC * 2;  // W bytes per chunk (two packed images)
+  constexpr int HB = BG_BM * WD_KC * 2;  // hidden bytes per chunk
+  constexpr int NW = 3, NH = 2;          // ring stages
+  constexpr int WI = WB / 4096;          // W DMAs per wave per chunk (1 KB each)
+  constexpr int HI = HB / 4096;          // hidden DMAs per wave per chunk
+  constexpr int VB = 8;                  // 16-row vocabulary blocks per wave
+  constexpr int MB = 8;                  // 16-row hidden blocks per wave
+  constexpr int CW = 32;                 // vocabulary columns per epilogue pass
+  constexpr int TSTR = CW + 4;           // floats per staged logit row
+  static_assert(128 * TSTR * 4 <= WB && 128 * TSTR * 4 <= HB, "half a pass fits in a stage");
+  static_assert(WI == VB && HI == VB, "one W and one hidden DMA per vocabulary block");
+  static_assert(NW * WB + NH * HB <= 160 * 1024, "the rings fit in 160 KB of LDS");
+  __shared__ __attribute__((aligned(1024))) unsigned char sm[NW * WB + NH * HB];
+  unsigned char *const sw = sm;
+  unsigned char *const sh = sm + NW * WB;
+
+  const PkMap map = pk_map(blockIdx.x, tiles_m);
+  if (map.stream < 0) return;
+  const int S = map.streams;
+  const int m0 = map.tm * BG_BM;
+  const int nkc = H / WD_KC;
+  const int items = map.stream < tiles_v ? (tiles_v - map.stream + S - 1) / S : 0;
+  const int Q = items * nkc;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wv = wave & 1;
+  const unsigned sbase = static_cast<unsigned>(reinterpret_cast<size_t>((__attribute__((address_space(3))) void *)sm));
+
+  // DMA source offsets: lane -> (row, slot) -> logical piece -> its place in
+  // the row-major packed image (W; waves 0-1 fill the first image's 128
+  // rows, waves 2-3 the second's) or the row-major hidden state (rows
+  // clamped to M - 1)
+  unsigned wo[WI], ho[HI];
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int r = 8 * (wave * WI + i) + (lane >> 3);
+    const int P = (lane & 7) ^ (r & 7);
+    wo[i] = static_cast<unsigned>((r & (PK_BV - 1)) * 128 + (P << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < HI; ++i) {
+    const int r = 8 * (wave * HI + i) + (lane >> 3);
+    const int P = (lane & 7) ^ (r & 7);
+    const int m = min(m0 + r, M - 1);
+    ho[i] = static_cast<unsigned>(m) * H * 2 + (P << 4);
+  }
+  // Sources and LDS targets of chunk j's W (W stage j % 3) and hidden rows
+  // (hidden stage j % 2).  A chunk past the last one (j >= Q) re-reads the
+  // last chunk into the stage it would use, which nothing reads again: the
+  // DMAs then need no branch, and the waits below stay the same every chunk.
+  struct Dma {
+    const unsigned char *src;
+    unsigned dst;
+  };
+  auto w_dma = [&](int j) {
+    const int jj = min(j, Q - 1);
+    const int item = jj / nkc;
+    const int kc = jj - item * nkc;
+    const int tv = map.stream + item * S;
+    const int img = min(tv * 2 + (wave >> 1), n_img - 1);
+    return Dma{wd_uniform(wpk + (static_cast<size_t>(img) * nkc + kc) * PK_IMG),
+               sbase + (j % NW) * WB + wave * WI * 1024};
+  };
+  auto h_dma = [&](int j) {
+    const int jj = min(j, Q - 1);
+    const int kc = jj - (jj / nkc) * nkc;
+    return Dma{wd_uniform(reinterpret_cast<const unsigned char *>(hidden) + kc * WD_KC * 2),
+               sbase + NW * WB + (j % NH) * HB + wave * HI * 1024};
+  };
+
+  // fragment offsets inside a stage: the swizzle depends on l16 only, so
+  // block b adds b * 16 rows of 128 bytes
+  int fa[2], fb[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    fa[s] = wd_piece(wv * 128 + l16, s * 4 + g);
+    fb[s] = wd_piece(wm * 128 + l16, s * 4 + g);
+  }
+  // (a wave whose rows all lie past M still runs its MFMAs, on the clamped
+  // rows; their logits are never screened)
+  graft::TopKeys<K> list;  // hidden row m0 + tid
+  list.init();
+
+  // prologue, in the order the waits below assume: W_0, H_0, W_1
+  if (Q > 0) {
+    const Dma w0 = w_dma(0), h0 = h_dma(0), w1 = w_dma(1);
+#pragma unroll
+    for (int i = 0; i < WI; ++i) lds_dma16_cached(w0.dst + i * 1024, w0.src, wo[i]);
+#pragma unroll
+    for (int i = 0; i < HI; ++i) lds_dma16_cached(h0.dst + i * 1024, h0.src, ho[i]);
+#pragma unroll
+    for (int i = 0; i < WI; ++i) lds_dma16_cached(w1.dst + i * 1024, w1.src, wo[i]);
+  }
+  int q = 0;
+  for (int item = 0; item < items; ++item) {
+    f32x4 acc[VB][MB];
+#pragma unroll
+    for (int a = 0; a < VB; ++a)
+#pragma unroll
+      for (int b = 0; b < MB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Both k-steps of a chunk in one straight run; each vocabulary fragment
+    // is read one block ahead of its MFMAs, and k-step 1's hidden fragments
+    // during k-step 0.  (The next chunks' DMAs are issued before, not among,
+    // the MFMAs: code paths that branch between MFMA groups make the
+    // register allocator move the 256 accumulators at every block edge.)
+    // The next chunks' DMAs (H_q+1 during k-step 0, W_q+2 during k-step 1)
+    // go one per vocabulary block among the MFMAs, so the memory pipeline
+    // takes them while the MFMAs run instead of stalling the wave at issue.
+    auto chunk = [&](const unsigned char *stw, const unsigned char *sth, const Dma hn, const Dma wn) {
+      auto fw = [&](int off) { return *reinterpret_cast<const bf16x8 *>(stw + off); };
+      auto fh = [&](int off) { return *reinterpret_cast<const bf16x8 *>(sth + off); };
+      bf16x8 b0[MB], b1[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) b0[mb] = fh(fb[0] + mb * 2048);
+      bf16x8 a = fw(fa[0]);
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        const bf16x8 an = vb + 1 < VB ? fw(fa[0] + (vb + 1) * 2048) : fw(fa[1]);
+        if (vb == VB / 2) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) b1[mb] = fh(fb[1] + mb * 2048);
+        }
+        lds_dma16_cached(hn.dst + vb * 1024, hn.src, ho[vb]);
+        __builtin_amdgcn_sched_barrier(0);  // the reads stay ahead of these MFMAs
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[vb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0[mb], acc[vb][mb], 0, 0, 0);
+        a = an;
+      }
+#pragma unroll
+      for (int vb = 0; vb < VB; ++vb) {
+        bf16x8 an = a;
+        if (vb + 1 < VB) an = fw(fa[1] + (vb + 1) * 2048);
+        lds_dma16_cached(wn.dst + vb * 1024, wn.src, wo[vb]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          acc[vb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1[mb], acc[vb][mb], 0, 0, 0);
+        a = an;
+      }
+    };
+    for (int kc = 0; kc < nkc; ++kc, ++q) {
+      // W_q and H_q have landed once only W_q+1 (issued after H_q) may be
+      // in flight; the barrier also ends every wave's reads of chunk q - 1,
+      // whose stages H_q+1 and W_q+2 now fill
+      ring_barrier<WI>();
+      chunk(sw + (q % NW) * WB, sh + (q % NH) * HB, h_dma(q + 1), w_dma(q + 2));
+    }
+
+    // ---- tile done: its logits go through the last chunk's two stages
+    // (rows 0-127 in the W stage, 128-255 in the hidden stage) in passes of
+    // 32 vocabulary columns
+    const int v0 = (map.stream + item * S) * BG_BV;
+    float *s_w = reinterpret_cast<float *>(sw + ((q - 1) % NW) * WB);
+    float *s_h = reinterpret_cast<float *>(sh + ((q - 1) % NH) * HB);
+    float *s_wave = wm == 0 ? s_w : s_h;  // this wave's rows
+    const float *src = (tid < 128 ? s_w : s_h) + (tid & 127) * TSTR;
+    const bool row_ok = m0 + tid < M;
+    __syncthreads();  // every wave is done reading the stages
+#pragma unroll
+    for (int p = 0; p < BG_BV / CW; ++p) {
+      if (wv == (p >> 2)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int vb = 2 * (p & 3) + h;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            // stored straight from the accumulation registers ("a")
+            const unsigned addr = static_cast<unsigned>(reinterpret_cast<size_t>(
+                (__attribute__((address_space(3))) float *)&s_wave[(mb * 16 + l16) * TSTR + h * 16 + 4 * g]));
+            asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "a"(acc[vb][mb]) : "memory");
+          }
+        }
+        // the compiler does not count the asm stores: wait for them here
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+      __syncthreads();
+      // Screening: a candidate bit per entry at least the row's k-th key
+      // value and at least the k-th largest of the pass's group maxima
+      // (groups of CW / K' entries, K' = max(k, 8) groups: K' entries of the
+      // pass are at least that large, so a smaller entry is not in the top
+      // k).  The inserts then run once per candidate of the lane with the
+      // most, not once per entry that any lane keeps.
+      const int c0 = v0 + p * CW;
+      float xv[CW];
+#pragma unroll
+      for (int u = 0; u < CW / 4; ++u) {
+        const float4 x = *reinterpret_cast<const float4 *>(src + 4 * u);
+        const int c = c0 + 4 * u;  // columns past V (zero rows of the last tile) never count
+        xv[4 * u] = c < V ? x.x : -INFINITY;
+        xv[4 * u + 1] = c + 1 < V ? x.y : -INFINITY;
+        xv[4 * u + 2] = c + 2 < V ? x.z : -INFINITY;
+        xv[4 * u + 3] = c + 3 < V ? x.w : -INFINITY;
+      }
+      constexpr int GS = CW / K;  // entries per group (4 for k <= 8 lists, 2 for 16)
+      float gmin = INFINITY;
+#pragma unroll
+      for (int gi = 0; gi < K; ++gi) {
+        float gm = xv[gi * GS];
+#pragma unroll
+        for (int e = 1; e < GS; ++e) gm = fmaxf(gm, xv[gi * GS + e]);
+        gmin = fminf(gmin, gm);
+      }
+      // with k < K only the k largest groups are needed; gmin then is
+      // smaller than needed, which keeps the bound valid
+      const float lk = list.k[K - 1] != 0 ? graft::key_value(list.k[K - 1]) : -INFINITY;
+      const float bound = fmaxf(lk, k == K ? gmin : -INFINITY);
+      uint32_t cand = 0;
+#pragma unroll
+      for (int j = 0; j < CW; ++j) cand |= static_cast<uint32_t>(!(xv[j] < bound) && c0 + j < V) << j;
+      if (!row_ok) cand = 0;
+      while (cand != 0) {
+        const int j = __builtin_ctz(cand);
+        cand &= cand - 1;
+        list.insert(graft::rank_key(src[j], c0 + j));
+      }
+      __syncthreads();  // the next pass overwrites the staged rows
+    }
+  }
+  // the DMAs past the last chunk must land before the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // this workgroup's k best keys of row m0 + tid (0 = no entry)
+  const int m = m0 + tid;
+  if (m < M) {
+    uint64_t *dst = part_out + (static_cast<size_t>(m) * S + map.stream) * k;
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (j < k) dst[j] = list.k[j];
+  }
+}
+
 }  // namespace
 
 namespace graft {
@@ -899,13 +1170,16 @@ size_t lmhead_fused_ws_bytes(int M, int V, int k) {
 namespace {
 int packed_tiles_m(int M) { return (M + BM - 1) / BM; }
 int wide_tiles_m(int M) { return (M + WD_BM - 1) / WD_BM; }
+int big_tiles_m(int M) { return (M + BG_BM - 1) / BG_BM; }
+// Above 128 rows the 256 x 256 tiles (128 flops per byte taken in).
+bool packed_big(int M) { return M > WD_BM; }
 // The fused packed path takes the wide tiles above 64 rows (65-128 rows:
 // one m tile, each W image read once; the 64-row kernel would run two m
 // tiles sharing each image through L2, about 3% slower).  Up to 64 rows
 // the 64-row kernel's 8 wavefronts stream W faster than 4.
 bool packed_wide(int M) { return M > BM; }
 size_t packed_fused_ws_bytes(int M, int k) {
-  const int T = packed_wide(M) ? wide_tiles_m(M) : packed_tiles_m(M);
+  const int T = packed_big(M) ? big_tiles_m(M) : (packed_wide(M) ? wide_tiles_m(M) : packed_tiles_m(M));
   if (packed_tiles_m(M) > PK_GRID) return 0;
   return static_cast<size_t>(M) * pk_map(0, T).streams * k * sizeof(uint64_t);
 }
@@ -988,6 +1262,21 @@ extern "C" int graft_lmhead_topk(int M, int H, int V, int k, const graft_bf16 *h
       hipLaunchKernelGGL((lmhead_packed_kernel<F, Kv, PK_WAVES, false>), dim3(PK_GRID), dim3(PK_WAVES * 64), 0, s, M, H, V,
                          F ? k : 0, hidden, wpk, F ? nullptr : logits, pk, tiles_m, tiles_v, 1.0f, nullptr, nullptr);
     };
+    if (fused && packed_big(M)) {
+      uint64_t *pk = static_cast<uint64_t *>(ws);
+      const int Tb = big_tiles_m(M);
+      const int n_img = (V + PK_BV - 1) / PK_BV;
+      const int tv = (V + BG_BV - 1) / BG_BV;
+      if (k <= 8)
+        hipLaunchKernelGGL((lmhead_big_kernel<8>), dim3(PK_GRID), dim3(256), 0, s, M, H, V, k, hidden, wpk, pk, Tb, tv,
+                           n_img);
+      else
+        hipLaunchKernelGGL((lmhead_big_kernel<16>), dim3(PK_GRID), dim3(256), 0, s, M, H, V, k, hidden, wpk, pk, Tb,
+                           tv, n_img);
+      int rc = graft::check_launch("lmhead (packed, 256 x 256 tiles, fused top-k)");
+      if (rc != GRAFT_OK) return rc;
+      return graft::launch_topk_merge(M, pk_map(0, Tb).streams, k, pk, topk_id, topk_val, s);
+    }
     if (fused && packed_wide(M)) {
       uint64_t *pk = static_cast<uint64_t *>(ws);
       const int Tw = wide_tiles_m(M);
@@ -1114,3 +1403,4 @@ extern "C" int graft_lmhead_topk_sample(int M, int H, int V, int k, float temper
   if (rc != GRAFT_OK) return rc;
   return graft::launch_topk_merge(M, S, 1, ps, sample_id, nullptr, s);
 }
+
