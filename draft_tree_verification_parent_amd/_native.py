@@ -28,6 +28,8 @@ SIGNATURES = {
     "graft_lmhead_topk_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),
     "graft_lmhead_topk": (c_int, [c_int, c_int, c_int, c_int, P, P, c_int, P, P, P, P, c_size_t, P]),
     "graft_lmhead_pack_bytes": (c_size_t, [c_int, c_int]),
+    "graft_lmhead_topk_noalloc_bytes": (c_size_t, [c_int, c_int]),
+    "graft_lmhead_topk_noalloc": (c_int, [c_int, c_int, c_int, c_int, P, P, P, P, P]),
     "graft_lmhead_pack": (c_int, [c_int, c_int, P, P, P]),
     "graft_accept": (c_int, [c_int, P, P, P, P, P, c_int, P, P, P, P, P]),
     "graft_lmhead_sample_workspace_bytes": (c_size_t, [c_int, c_int, c_int]),

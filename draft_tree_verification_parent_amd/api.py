@@ -110,6 +110,18 @@ def graft_lmhead_topk(M, H, V, k, hidden, w, logits, topk_id=None, topk_val=None
                 _s(stream))
 
 
+def graft_lmhead_topk_noalloc_bytes(M, k):
+    return int(N.lib().graft_lmhead_topk_noalloc_bytes(int(M), int(k)))
+
+
+def graft_lmhead_topk_noalloc(M, H, V, k, hidden, w_packed, topk_id, topk_val=None, stream=None):
+    """Fused packed lm-head + top-k with the library's built-in scratch (no
+    workspace argument; the call allocates nothing)."""
+    return call("graft_lmhead_topk_noalloc", int(M), int(H), int(V), int(k), _p(hidden, "bf16", "hidden"),
+                _p(w_packed, "bf16", "w_packed"), _p(topk_id, "i32", "topk_id"), _p(topk_val, "f32", "topk_val"),
+                _s(stream))
+
+
 def graft_lmhead_pack_bytes(V, H):
     return int(N.lib().graft_lmhead_pack_bytes(V, H))
 

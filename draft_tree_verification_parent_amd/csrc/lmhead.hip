@@ -33,6 +33,7 @@
 // on the split).  In the packed path the lists persist across a
 // workgroup's tiles, so the merge reads one list per (row, workgroup).
 #include <climits>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1404,3 +1405,57 @@ extern "C" int graft_lmhead_topk_sample(int M, int H, int V, int k, float temper
   return graft::launch_topk_merge(M, S, 1, ps, sample_id, nullptr, s);
 }
 
+// ------------------------------------------------- no-allocation variant
+// graft_lmhead_topk's fused packed mode with its workspace (the per-(row,
+// workgroup) candidate lists the merge reads) in a file-scope device array
+// instead of a caller buffer, for callers that cannot allocate.  Each GPU
+// holds its own copy of the array; its address is taken once per device with
+// that device current and kept.  Every list the merge reads is written by the
+// same call, so nothing needs clearing; calls that overlap on one GPU share
+// the array and race.
+namespace {
+constexpr size_t kNoAllocScratchBytes = GRAFT_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this device's scratch array (nullptr + message on failure).
+void *scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" size_t graft_lmhead_topk_noalloc_bytes(int M, int k) {
+  if (M <= 0 || k < 1 || k > GRAFT_MAX_K || packed_tiles_m(M) > PK_GRID) return 0;
+  return packed_fused_ws_bytes(M, k);
+}
+
+extern "C" int graft_lmhead_topk_noalloc(int M, int H, int V, int k, const graft_bf16 *hidden,
+                                         const graft_bf16 *w_packed, int32_t *topk_id, float *topk_val,
+                                         graft_stream stream) {
+  using graft::fail;
+  if (M < 0 || V <= 0 || k < 1 || k > GRAFT_MAX_K || k > V)
+    return fail(GRAFT_EINVAL, "lmhead_topk_noalloc: M=%d V=%d k=%d", M, V, k);
+  if (!hidden || !w_packed || !topk_id) return fail(GRAFT_EINVAL, "lmhead_topk_noalloc: NULL array");
+  if (packed_tiles_m(M) > PK_GRID)
+    return fail(GRAFT_EINVAL, "lmhead_topk_noalloc: M=%d exceeds the packed path's %d rows", M, PK_GRID * BM);
+  const size_t need = packed_fused_ws_bytes(M, k);
+  if (need > kNoAllocScratchBytes)
+    return fail(GRAFT_EINVAL, "lmhead_topk_noalloc: M=%d, k=%d need %zu bytes of scratch, above the %zu built in", M,
+                k, need, kNoAllocScratchBytes);
+  if (M == 0) return GRAFT_OK;
+  void *ws = scratch_on_current_device();
+  if (!ws) return fail(GRAFT_EHIP, "lmhead_topk_noalloc: no scratch address on the current device");
+  return graft_lmhead_topk(M, H, V, k, hidden, w_packed, GRAFT_W_PACKED, nullptr, topk_id, topk_val, ws,
+                           kNoAllocScratchBytes, stream);
+}

@@ -334,6 +334,24 @@ int graft_lmhead_topk(int M, int H, int V, int k,
                       graft_stream stream);
 
 /*
+ * graft_lmhead_topk without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the fused packed mode (hidden given,
+ * logits not materialised, w_packed from graft_lmhead_pack, H % 128 == 0)
+ * with its scratch (the per-(row, workgroup) candidate lists) in an array
+ * built into the library, GRAFT_NOALLOC_SCRATCH_BYTES per GPU, held until the
+ * process ends.  graft_lmhead_topk_noalloc_bytes(M, k) is the scratch a call
+ * needs (at most 8 MiB for M <= 16384 and k <= 16 with the current tilings;
+ * 960 rows at k = 8 need 3.75 MiB); a call that needs more returns
+ * GRAFT_EINVAL.  Results equal graft_lmhead_topk's bit for bit.  The call
+ * allocates nothing; calls that overlap on one GPU share its array and race.
+ */
+#define GRAFT_NOALLOC_SCRATCH_BYTES (8u << 20)
+size_t graft_lmhead_topk_noalloc_bytes(int M, int k);
+int graft_lmhead_topk_noalloc(int M, int H, int V, int k, const graft_bf16 *hidden, const graft_bf16 *w_packed,
+                              int32_t *topk_id, float *topk_val, graft_stream stream);
+
+/*
  * Weight packing for graft_lmhead_topk (done once, when the lm-head is
  * loaded; not part of a round).  w (device bf16 [V, H] row-major) is
  * rewritten into w_packed (device, graft_lmhead_pack_bytes(V, H) bytes,
