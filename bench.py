@@ -251,8 +251,11 @@ def measure(cfg, steps, warmup, with_cpu, extras):
     lm_flops = 2.0 * M * H * V
     lm_s = step_us["lmhead_topk"] * 1e-6
     wide = M > 64
-    kern = (f"lmhead_wide_kernel + topk_merge_kernel<{8 if ri.k <= 8 else 16}> (one graft_lmhead_topk call, "
-            f"packed weights, {M} rows)" if wide else
+    kk = 8 if ri.k <= 8 else 16
+    kern = (f"lmhead_big_kernel<{kk}> + topk_merge_kernel<{kk}> (one graft_lmhead_topk call, packed weights, "
+            f"{M} rows, 256 x 256 tiles)" if M > 128 else
+            f"lmhead_wide_kernel + topk_merge_kernel<{kk}> (one graft_lmhead_topk call, packed weights, {M} rows)"
+            if wide else
             f"lmhead_packed_kernel<true,{8 if ri.k <= 8 else 16},8> + topk_merge_kernel<{8 if ri.k <= 8 else 16}> "
             f"(one graft_lmhead_topk call, packed weights)")
     traffic = measured_traffic(f"cfg{cfg}")

@@ -915,6 +915,51 @@ __global__ __launch_bounds__(256, 1) void lmhead_wide_kernel(int M, int H, int V
 // against its own k-th key.  One list per (row, workgroup) is written at the
 // end and merged by topk_merge_kernel.  The MFMA sums run in the k-order of
 // every other path, so the logits are bit-identical.
+// A sorted list of K (value, id) keys whose compare-exchanges are two
+// fp64 instructions.  Key bits: order(value) << 30 | (2^30 - 1 - id): the
+// top two bits are clear, so as an fp64 bit pattern every key is a finite
+// non-negative number (subnormal for the smallest orders; fp64 subnormals
+// are not flushed) and fp64 order equals the integer order of the bits, the
+// (value desc, id asc) ranking.  0.0 is the empty slot.  Ids below 2^30 - 1.
+template <int K>
+struct F64Keys {
+  double k[K];
+  __device__ void init() {
+#pragma unroll
+    for (int j = 0; j < K; ++j) k[j] = 0.0;
+  }
+  __device__ static double make(float v, int id) {
+    const uint64_t bits = (static_cast<uint64_t>(graft::float_order(v)) << 30) |
+                          static_cast<uint64_t>((1u << 30) - 1u - static_cast<uint32_t>(id));
+    return __longlong_as_double(static_cast<long long>(bits));
+  }
+  // the K-th key's value (-inf while the list has an empty slot)
+  __device__ float kth_value() const {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(k[K - 1]));
+    return b == 0 ? -INFINITY : graft::key_value(static_cast<uint64_t>(static_cast<uint32_t>(b >> 30)) << 32);
+  }
+  // branch-free insertion: x bubbles down the descending list (0.0, the
+  // empty key, leaves it unchanged).  One v_max_f64 and one v_min_f64 per
+  // slot, written out: the library calls would add two canonicalising
+  // operations each, and no key is a NaN.
+  __device__ void insert(double x) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      double hi, lo;
+      asm("v_max_f64 %0, %2, %3\n\tv_min_f64 %1, %2, %3" : "=&v"(hi), "=&v"(lo) : "v"(k[j]), "v"(x));
+      k[j] = hi;
+      x = lo;
+    }
+  }
+  // the key of slot j in the rank_key format the merge reads (0 = empty)
+  __device__ uint64_t rank_key(int j) const {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(k[j]));
+    if (b == 0) return 0;
+    const uint32_t id = (1u << 30) - 1u - static_cast<uint32_t>(b & ((1u << 30) - 1u));
+    return (static_cast<uint64_t>(static_cast<uint32_t>(b >> 30)) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - id);
+  }
+};
+
 constexpr int BG_BM = 256;  // hidden rows per tile
 constexpr int BG_BV = 256;  // vocabulary rows per tile
 
@@ -1008,7 +1053,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(int M, int H, int V,
   }
   // (a wave whose rows all lie past M still runs its MFMAs, on the clamped
   // rows; their logits are never screened)
-  graft::TopKeys<K> list;  // hidden row m0 + tid
+  F64Keys<K> list;  // hidden row m0 + tid
   list.init();
 
   // prologue, in the order the waits below assume: W_0, H_0, W_1
@@ -1039,10 +1084,17 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(int M, int H, int V,
     auto chunk = [&](const unsigned char *stw, const unsigned char *sth, const Dma hn, const Dma wn) {
       auto fw = [&](int off) { return *reinterpret_cast<const bf16x8 *>(stw + off); };
       auto fh = [&](int off) { return *reinterpret_cast<const bf16x8 *>(sth + off); };
+      // the first MFMA needs only the first vocabulary fragment and the
+      // first hidden one: those are read first
       bf16x8 b0[MB], b1[MB];
+      bf16x8 a = fw(fa[0]);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) b0[mb] = fh(fb[0] + mb * 2048);
-      bf16x8 a = fw(fa[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      // the hidden rows of the next chunk have one chunk of lead time: all
+      // at once, first
+#pragma unroll
+      for (int i = 0; i < HI; ++i) lds_dma16_cached(hn.dst + i * 1024, hn.src, ho[i]);
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
         const bf16x8 an = vb + 1 < VB ? fw(fa[0] + (vb + 1) * 2048) : fw(fa[1]);
@@ -1050,7 +1102,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(int M, int H, int V,
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) b1[mb] = fh(fb[1] + mb * 2048);
         }
-        lds_dma16_cached(hn.dst + vb * 1024, hn.src, ho[vb]);
+        if (vb & 1) lds_dma16_cached(wn.dst + (vb >> 1) * 1024, wn.src, wo[vb >> 1]);
         __builtin_amdgcn_sched_barrier(0);  // the reads stay ahead of these MFMAs
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -1061,7 +1113,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(int M, int H, int V,
       for (int vb = 0; vb < VB; ++vb) {
         bf16x8 an = a;
         if (vb + 1 < VB) an = fw(fa[1] + (vb + 1) * 2048);
-        lds_dma16_cached(wn.dst + vb * 1024, wn.src, wo[vb]);
+        if (vb & 1) lds_dma16_cached(wn.dst + (4 + (vb >> 1)) * 1024, wn.src, wo[4 + (vb >> 1)]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -1106,43 +1158,71 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(int M, int H, int V,
       }
       __syncthreads();
       // Screening: a candidate bit per entry at least the row's k-th key
-      // value and at least the k-th largest of the pass's group maxima
-      // (groups of CW / K' entries, K' = max(k, 8) groups: K' entries of the
-      // pass are at least that large, so a smaller entry is not in the top
-      // k).  The inserts then run once per candidate of the lane with the
-      // most, not once per entry that any lane keeps.
+      // value; in the workgroup's first pass, while the lists are still
+      // empty, also at least the k-th largest of the pass's group maxima
+      // (K groups of CW / K entries: K entries of the pass are at least that
+      // large, so a smaller entry is not in the top k; with k < K the bound
+      // is lower than needed, still valid).  After that pass every list is
+      // full.  Columns past V (zero rows of the last tile) never count.  The
+      // inserts then run once per candidate of the lane with the most, not
+      // once per entry that any lane keeps.
       const int c0 = v0 + p * CW;
-      float xv[CW];
-#pragma unroll
-      for (int u = 0; u < CW / 4; ++u) {
-        const float4 x = *reinterpret_cast<const float4 *>(src + 4 * u);
-        const int c = c0 + 4 * u;  // columns past V (zero rows of the last tile) never count
-        xv[4 * u] = c < V ? x.x : -INFINITY;
-        xv[4 * u + 1] = c + 1 < V ? x.y : -INFINITY;
-        xv[4 * u + 2] = c + 2 < V ? x.z : -INFINITY;
-        xv[4 * u + 3] = c + 3 < V ? x.w : -INFINITY;
-      }
-      constexpr int GS = CW / K;  // entries per group (4 for k <= 8 lists, 2 for 16)
-      float gmin = INFINITY;
-#pragma unroll
-      for (int gi = 0; gi < K; ++gi) {
-        float gm = xv[gi * GS];
-#pragma unroll
-        for (int e = 1; e < GS; ++e) gm = fmaxf(gm, xv[gi * GS + e]);
-        gmin = fminf(gmin, gm);
-      }
-      // with k < K only the k largest groups are needed; gmin then is
-      // smaller than needed, which keeps the bound valid
-      const float lk = list.k[K - 1] != 0 ? graft::key_value(list.k[K - 1]) : -INFINITY;
-      const float bound = fmaxf(lk, k == K ? gmin : -INFINITY);
       uint32_t cand = 0;
+      auto screen = [&](auto first_tag, auto tail_tag) {
+        constexpr bool FIRST = decltype(first_tag)::value;
+        constexpr bool TAIL = decltype(tail_tag)::value;
+        float xv[CW];
 #pragma unroll
-      for (int j = 0; j < CW; ++j) cand |= static_cast<uint32_t>(!(xv[j] < bound) && c0 + j < V) << j;
+        for (int u = 0; u < CW / 4; ++u) {
+          const float4 x = *reinterpret_cast<const float4 *>(src + 4 * u);
+          xv[4 * u] = x.x;
+          xv[4 * u + 1] = x.y;
+          xv[4 * u + 2] = x.z;
+          xv[4 * u + 3] = x.w;
+        }
+        if constexpr (TAIL) {
+#pragma unroll
+          for (int e = 0; e < CW; ++e) xv[e] = c0 + e < V ? xv[e] : -INFINITY;
+        }
+        float bound = list.kth_value();
+        if constexpr (FIRST) {
+          constexpr int GS = CW / K;  // entries per group (4 for k <= 8 lists, 2 for 16)
+          float gmin = INFINITY;
+#pragma unroll
+          for (int gi = 0; gi < K; ++gi) {
+            float gm = xv[gi * GS];
+#pragma unroll
+            for (int e = 1; e < GS; ++e) gm = fmaxf(gm, xv[gi * GS + e]);
+            gmin = fminf(gmin, gm);
+          }
+          if (k == K) bound = fmaxf(bound, gmin);
+        }
+#pragma unroll
+        for (int e = 0; e < CW; ++e) {
+          bool keep = !(xv[e] < bound);
+          if constexpr (TAIL) keep = keep && c0 + e < V;
+          cand |= static_cast<uint32_t>(keep) << e;
+        }
+      };
+      const bool first = item == 0 && p == 0;  // uniform
+      const bool tail = v0 + BG_BV > V;         // uniform
+      if (first) {
+        if (tail) screen(std::true_type{}, std::true_type{});
+        else screen(std::true_type{}, std::false_type{});
+      } else {
+        if (tail) screen(std::false_type{}, std::true_type{});
+        else screen(std::false_type{}, std::false_type{});
+      }
       if (!row_ok) cand = 0;
-      while (cand != 0) {
-        const int j = __builtin_ctz(cand);
+      // as many rounds as the lane with the most candidates, every lane in
+      // every round (a lane with none left inserts the empty key): no
+      // divergent branches
+      const uint32_t rounds = graft::wave_max_u32(static_cast<uint32_t>(__popc(cand)));
+      for (uint32_t r = 0; r < rounds; ++r) {
+        const int j = cand != 0 ? __builtin_ctz(cand) : 0;
+        const double key = cand != 0 ? F64Keys<K>::make(src[j], c0 + j) : 0.0;
         cand &= cand - 1;
-        list.insert(graft::rank_key(src[j], c0 + j));
+        list.insert(key);
       }
       __syncthreads();  // the next pass overwrites the staged rows
     }
@@ -1155,7 +1235,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(int M, int H, int V,
     uint64_t *dst = part_out + (static_cast<size_t>(m) * S + map.stream) * k;
 #pragma unroll
     for (int j = 0; j < K; ++j)
-      if (j < k) dst[j] = list.k[j];
+      if (j < k) dst[j] = list.rank_key(j);
   }
 }
 
