@@ -5,9 +5,10 @@
 //
 // Query row (node i, head h) sees cache slots 0..ctx-1 and tree slot ctx+j
 // iff bit j of mask[i].  All N tree nodes times the G = Hq/Hkv heads of one
-// KV head share every K/V tile, so one workgroup owns one (request, KV head,
-// key split) and all of its N*G query rows: K/V are read from HBM once per
-// split, and both products run on MFMA:
+// KV head share every K/V tile, so a workgroup takes a key range of one
+// (request, KV head) for up to 384 of its query rows at once (all N*G of
+// them up to N*G = 384, the case of a 64-node tree with G <= 6): each K/V
+// chunk is read from HBM once per row group, and both products run on MFMA:
 //   S^T = K . Q^T   (A = K tile from LDS, B = Q fragments kept in registers)
 //   O^T = V^T . P^T (A = V^T fragments from LDS, B = P straight from the S^T
 //                    accumulators, re-packed to bf16)
@@ -26,10 +27,13 @@
 // 16-lane transpose turns 4 keys x 16 head-dim columns of V into each lane
 // holding 4 keys of one column (two reads per fragment).
 //
-// The key range is split over workgroups (8 KV heads alone cannot fill 256
-// CUs); each split writes unnormalised O, the running max and the exp-sum,
-// and a merge kernel combines splits with the usual log-sum-exp weights.
-// With a single split the workgroup normalises and writes bf16 directly.
+// Work is dealt stream-K: the 64-key chunks of all (request, KV head, row
+// group) units form one sequence cut into equal ranges, one per workgroup,
+// so that ragged context lengths do not leave CUs idle behind the longest
+// request and a few KV heads still fill 256 CUs.  A unit whose chunks one
+// workgroup covers is normalised and written as bf16 there; a unit cut by a
+// range boundary leaves unnormalised O, the running max and the exp-sum per
+// piece, which a merge kernel combines with the usual log-sum-exp weights.
 #include <cmath>
 #include <type_traits>
 
@@ -47,7 +51,8 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int KCH = 64;      // keys per staged chunk (four 16-key MFMA blocks)
 constexpr int NS = 4;        // LDS ring stages (128 KB at d = 128: one workgroup per CU)
-constexpr int MIN_SPLIT = 128;
+constexpr int MIN_CHUNKS = 2;        // fewest chunks a workgroup is given
+constexpr int kMaxWorkgroups = 256;  // one per CU
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -126,11 +131,12 @@ struct Params {
   int max_n;
   const int32_t *row_off;
   const uint64_t *mask;
-  int split_len, nsplit, rows_per_wg, row_groups, rows_cap;
+  int nwg, rows_per_wg, row_groups, slot_rows;
   graft_bf16 *out;
   float *lse;
-  float *ws_o;
-  float *ws_ml;
+  float *ws_o;     // [2 nwg][slot_rows][D] partial O (unnormalised)
+  float *ws_ml;    // [2 nwg][slot_rows][2] partial (running max, exp-sum)
+  int32_t *ws_pre; // [B + 1] chunk offsets of the requests, written by workgroup 0
   int32_t *err;
 };
 
@@ -148,13 +154,26 @@ struct Request {
   int64_t kv_off;
 };
 
-// Loads the request's scalars and returns false (flagging once) when its
-// lengths exceed the bounds the grid was sized for or its row capacity, or
-// its K/V offset is not a multiple of 8 elements (K/V rows are copied 16
-// bytes at a time from kv_off[b] on).  All five loads are issued together:
-// with short-circuit tests, or a flag branch between them, each would wait
-// for the one before, a chain of round trips ahead of the first K/V copy.
-__device__ inline bool request_ok(const Params &P, int b, Request &q) {
+// False when the request's lengths exceed the bounds the launch was sized
+// for or its row capacity, or its K/V offset is not a multiple of 8
+// elements (K/V rows are copied 16 bytes at a time from kv_off[b] on);
+// report: raise the matching error flag.
+__device__ inline bool request_valid(const Params &P, const Request &q, int r_end, bool report) {
+  const bool ok = (q.ctx >= 0) & (q.ctx <= P.max_ctx) & (q.n >= 1) & (q.n <= P.max_n) &
+                  (q.n <= GRAFT_MAX_NODES) & (q.n <= r_end - q.r_off);
+  const bool aligned = (q.kv_off & 7) == 0;
+  if (report) {
+    if (!ok) graft::raise_flag(P.err, GRAFT_ERR_CAPACITY);
+    if (!aligned) graft::raise_flag(P.err, GRAFT_ERR_ALIGN);
+  }
+  return ok & aligned;
+}
+
+// Loads the scalars of request b (b wave-uniform) and validates them
+// (report: raise the error flags).  All five loads are issued together:
+// with short-circuit tests between them, each would wait for the one
+// before, a chain of round trips ahead of the first K/V copy.
+__device__ inline bool request_ok(const Params &P, int b, Request &q, bool report = false) {
   q.kv_off = ld_scalar(P.kv_off + b);
   q.ctx = ld_scalar(P.ctx_len + b);
   q.n = ld_scalar(P.n + b);
@@ -164,41 +183,32 @@ __device__ inline bool request_ok(const Params &P, int b, Request &q) {
   // issued before the single wait for them
   asm volatile("" ::"s"(q.kv_off), "s"(q.ctx), "s"(q.n), "s"(q.r_off), "s"(r_end));
   __builtin_amdgcn_sched_barrier(0);
-  const bool ok = (q.ctx >= 0) & (q.ctx <= P.max_ctx) & (q.n >= 1) & (q.n <= P.max_n) &
-                  (q.n <= GRAFT_MAX_NODES) & (q.n <= r_end - q.r_off);
-  const bool aligned = (q.kv_off & 7) == 0;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-    if (!ok) graft::raise_flag(P.err, GRAFT_ERR_CAPACITY);
-    if (!aligned) graft::raise_flag(P.err, GRAFT_ERR_ALIGN);
-  }
-  return ok & aligned;
+  return request_valid(P, q, r_end, report);
 }
 
+// One segment: keys [k_begin, k_end) of unit (request b, KV head h, row
+// group rg) for all of the unit's query rows.  full: the segment is the
+// unit's whole key range, and the normalised bf16 output (and LSE) is
+// written; otherwise the unnormalised partial (O, running max, exp-sum) goes
+// to workspace slot `slot`.  Every thread of the workgroup calls it.
 template <int D, int RBW>
-__global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
+__device__ __forceinline__ void attend_segment(const Params &P, unsigned char *sm, int b, int h, int rg,
+                                               const Request &q, int k_begin, int k_end, bool full, int slot) {
   using TL = Tile<D>;
   constexpr int DS = D / 32;  // MFMA k-steps over the head dim
   constexpr int DB = D / 16;  // 16-wide output blocks over the head dim
   constexpr int DI = TL::DI;
-  __shared__ __attribute__((aligned(1024))) unsigned char sm[NS * TL::SB];
 
-  const int b = blockIdx.z;
-  const int h = blockIdx.y / P.row_groups;
-  const int rg = blockIdx.y - h * P.row_groups;
-  const int split = blockIdx.x;
-  Request q;
-  if (!request_ok(P, b, q)) return;
   const int ctx = q.ctx, n = q.n;
-  const int L = ctx + n;
-  const int k_begin = split * P.split_len;
-  if (k_begin >= L) return;
-  const int k_end = min(L, k_begin + P.split_len);
   const int rows_total = n * P.G;
   const int row_lo = rg * P.rows_per_wg;
   if (row_lo >= rows_total) return;
   const int nch = (k_end - k_begin + KCH - 1) / KCH;
 
-  const int tid = threadIdx.x;
+  // the lane-dependent offsets below are recomputed per segment rather than
+  // hoisted out of the segment loop, where they would stay live across it
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l16 = lane & 15;
@@ -455,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
     const float l_tot = group4_sum(l_run[j]);
     if (!rvalid[j]) continue;
     const int r = row_lo + (j * kWaves + wave) * 16 + l16;
-    if (P.nsplit == 1) {
+    if (full) {
       const int node = r / P.G;
       const int hq = h * P.G + (r - node * P.G);
       const size_t orow = static_cast<size_t>(r_off + node) * P.Hq + hq;
@@ -469,21 +479,205 @@ __global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
       }
       if (P.lse && g == 0) P.lse[orow] = (m_run[j] + log2f(l_tot)) * kLn2;
     } else {
-      const size_t slot = ((static_cast<size_t>(b) * P.Hkv + h) * P.nsplit + split) * P.rows_cap + r;
+      const size_t srow = static_cast<size_t>(slot) * P.slot_rows + (r - row_lo);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<f32x4 *>(P.ws_o + slot * D + db * 16 + 4 * g) = oacc[j][db];
+        *reinterpret_cast<f32x4 *>(P.ws_o + srow * D + db * 16 + 4 * g) = oacc[j][db];
       if (g == 0) {
-        P.ws_ml[slot * 2] = m_run[j];
-        P.ws_ml[slot * 2 + 1] = l_tot;
+        P.ws_ml[srow * 2] = m_run[j];
+        P.ws_ml[srow * 2 + 1] = l_tot;
       }
     }
   }
 }
 
-// Combines the splits of one (request, KV head, query row): D/4 lanes per
-// row, each owning 4 head-dim columns; one pass with a running maximum, the
-// split loads unrolled so their latencies overlap.
+// A unit is one (KV head, row group) of a request that has rows in that
+// group: Hkv * ceil(n G / rows_per_wg) units, taken KV head by KV head, each
+// of ceil((ctx + n) / 64) chunks (a request skipped as invalid has none).
+__device__ inline int unit_chunks(const Request &q, bool ok) { return ok ? (q.ctx + q.n + KCH - 1) / KCH : 0; }
+__device__ inline int live_groups(const Params &P, const Request &q) {
+  return (q.n * P.G + P.rows_per_wg - 1) / P.rows_per_wg;
+}
+
+// The requests' chunk offsets (a workgroup scan over their lengths, into
+// s_pre; workgroup 0 also stores them for the merge and raises the
+// requests' error flags), and where workgroup w's range starts: out = {T,
+// the request b holding chunk s_w, s_w - s_pre[b]}.  Thread t owns requests
+// t * PT .. t * PT + PT - 1; a wave scan of the owners' sums and a scan of
+// the wave totals give each owner its starting offset.  Loops here are
+// fully unrolled: a loop ahead of the segment loop changed how the
+// segments' registers were allocated and pushed the 3-row-block variant
+// into spills.
+__device__ inline void stream_start(const Params &P, int *s_pre, int *s_wsum, int *out) {
+  constexpr int PT = (GRAFT_ATTN_MAX_BATCH + kThreads - 1) / kThreads;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int b = tid * PT + i;
+    if (b < P.B) {
+      Request q;
+      q.kv_off = P.kv_off[b];
+      q.ctx = P.ctx_len[b];
+      q.n = P.n[b];
+      q.r_off = P.row_off[b];
+      const bool ok = request_valid(P, q, P.row_off[b + 1], blockIdx.x == 0);
+      const int cnt = unit_chunks(q, ok) * P.Hkv * live_groups(P, q);
+      s_pre[b] = cnt;
+      mine += cnt;
+    }
+  }
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - mine;
+#pragma unroll
+  for (int w2 = 0; w2 < kWaves; ++w2) run += w2 < wave ? s_wsum[w2] : 0;
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int b = tid * PT + i;
+    if (b < P.B) {
+      const int cnt = s_pre[b];
+      s_pre[b] = run;
+      run += cnt;
+    }
+  }
+  if (tid == kThreads - 1) s_pre[P.B] = run;  // run: the total T
+  __syncthreads();
+  const int T = s_pre[P.B];
+  if (blockIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int b = tid * PT + i;
+      if (b <= P.B) P.ws_pre[b] = s_pre[b];
+    }
+  }
+  const int s_w = static_cast<int>(static_cast<long long>(blockIdx.x) * T / P.nwg);
+  // the request holding chunk s_w: s_pre[b] <= s_w < s_pre[b + 1] (one
+  // request, when s_w < T)
+#pragma unroll
+  for (int i = 0; i < PT; ++i) {
+    const int b = tid * PT + i;
+    if (b < P.B && s_pre[b] <= s_w && s_w < s_pre[b + 1]) {
+      out[1] = b;
+      out[2] = s_w - s_pre[b];
+    }
+  }
+  if (tid == 0) out[0] = T;
+}
+
+// Stream-K over the chunk sequence: the units (request, KV head, row group)
+// in order, each ceil((ctx + n) / 64) chunks long.  Workgroup w of nwg takes
+// chunks [w T / nwg, (w + 1) T / nwg) of the T in all, so every workgroup
+// gets the same number of chunks whatever the requests' lengths.  A unit
+// that one workgroup covers whole is finished there; a unit cut by a range
+// boundary leaves partials (at most two per workgroup, its first and its
+// last segment: slots 2w and 2w + 1) that tree_attn_merge_kernel combines.
+// The per-request chunk offsets come from a workgroup scan over the
+// requests' lengths, kept in the (not yet used) ring LDS; workgroup 0 also
+// stores them for the merge and raises the requests' error flags.
+template <int D, int RBW>
+__global__ __launch_bounds__(kThreads, 2) void tree_attn_kernel(Params P) {
+  using TL = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char sm[NS * TL::SB];
+  __shared__ int s_wsum[kWaves];
+  static_assert(NS * TL::SB >= 4 * (GRAFT_ATTN_MAX_BATCH + 1), "request offsets fit the ring");
+  int *s_pre = reinterpret_cast<int *>(sm);
+  const int tid = threadIdx.x;
+
+  // where this workgroup's range starts: chunk s_w, in request b at offset
+  // o.  One request needs no scan.
+  __shared__ int s_start[3];
+  int T;
+  if (P.B == 1) {
+    Request q;
+    const bool ok = request_ok(P, 0, q, blockIdx.x == 0 && tid == 0);
+    T = unit_chunks(q, ok) * P.Hkv * live_groups(P, q);
+    if (blockIdx.x == 0 && tid == 0) {
+      P.ws_pre[0] = 0;
+      P.ws_pre[1] = T;
+    }
+  } else {
+    stream_start(P, s_pre, s_wsum, s_start);
+    __syncthreads();
+    T = __builtin_amdgcn_readfirstlane(s_start[0]);
+  }
+  const int w = blockIdx.x;
+  const int s_w = static_cast<int>(static_cast<long long>(w) * T / P.nwg);
+  const int e_w = static_cast<int>(static_cast<long long>(w + 1) * T / P.nwg);
+  if (s_w >= e_w) return;
+  int b = 0, o = s_w;
+  if (P.B != 1) {
+    b = __builtin_amdgcn_readfirstlane(s_start[1]);
+    o = __builtin_amdgcn_readfirstlane(s_start[2]);
+    __syncthreads();  // every wave has read s_pre before the ring overwrites it
+  }
+
+  // The walk's next state (request, unit, position) waits in LDS while a
+  // segment runs, so that no register is held across the segment for it
+  // (the request's scalars are loaded again per segment: scalar-cache
+  // hits).  Two copies, by segment parity: thread 0 writes the next
+  // segment's copy while slower waves may still be reading this one (the
+  // barriers inside a segment then order the copy they read against its
+  // next rewrite).
+  __shared__ int s_walk[2][4];
+  int ui, c, gpos = s_w, par = 0;
+  {
+    Request q;
+    const int nch = unit_chunks(q, request_ok(P, b, q));  // the request holds chunk s_w
+    ui = o / nch;
+    c = o - ui * nch;
+  }
+  for (;;) {
+    Request q;
+    const int nch = unit_chunks(q, request_ok(P, b, q));  // > 0: the request holds chunk gpos
+    const int rgl = live_groups(P, q);
+    const int len = min(e_w - gpos, nch - c);
+    const int h = ui / rgl;
+    const int rg = ui - h * rgl;
+    const int L = q.ctx + q.n;
+    volatile int *walk = s_walk[par];
+    if (tid == 0) {
+      // the next unit: the next (KV head, row group), else the next request
+      // with chunks (the walk stops before passing the last)
+      int nb = b, nu = ui + 1;
+      if (nu == P.Hkv * rgl) {
+        nu = 0;
+        ++nb;
+      }
+      walk[0] = nb;
+      walk[1] = nu;
+      walk[2] = gpos + len;
+    }
+    attend_segment<D, RBW>(P, sm, b, h, rg, q, c * KCH, min(L, (c + len) * KCH), c == 0 && len == nch,
+                           2 * w + (gpos == s_w ? 0 : 1));
+    __syncthreads();  // every wave is done with the ring before it refills; walk[] is written
+    gpos = __builtin_amdgcn_readfirstlane(walk[2]);
+    if (gpos >= e_w) break;
+    b = __builtin_amdgcn_readfirstlane(walk[0]);
+    ui = __builtin_amdgcn_readfirstlane(walk[1]);
+    c = 0;
+    par ^= 1;
+    if (ui == 0)  // skip requests without chunks (invalid ones)
+      while (unit_chunks(q, request_ok(P, b, q)) == 0) ++b;
+  }
+  // the ring's last DMAs were waited for inside the segment
+}
+
+// Combines the partials of the units that no single workgroup covered, one
+// query row of one KV head per D/4 lanes, each lane owning 4 head-dim
+// columns: the workgroups over the unit are the non-empty ones from the
+// one holding its first chunk to the one holding its last; the first uses
+// its second slot when its range began before the unit, every other one its
+// first slot.  One pass with a running
+// maximum, the slot loads unrolled so that their latencies overlap.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_merge_kernel(Params P) {
   constexpr int TPR = D / 4;      // threads per row
@@ -495,30 +689,50 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(Params P) {
   Request q;
   if (!request_ok(P, b, q)) return;
   if (r >= q.n * P.G) return;
-  const int L = q.ctx + q.n;
-  const int ns = (L + P.split_len - 1) / P.split_len;
-  const size_t base = (static_cast<size_t>(b) * P.Hkv + h) * P.nsplit * P.rows_cap + r;
+  const int nch = unit_chunks(q, true);
+  const int rg = r / P.rows_per_wg;
+  // the chunk count and the unit's first chunk (one request: no loads)
+  const int rgl = live_groups(P, q);
+  const int T = P.B == 1 ? P.Hkv * rgl * nch : P.ws_pre[P.B];
+  const int A = (P.B == 1 ? 0 : P.ws_pre[b]) + (h * rgl + rg) * nch;
+  // The offsets come from the attention kernel of the same call; whatever
+  // they hold, every slot read below stays inside the 2 nwg slots.
+  if (T <= 0 || A < 0 || A > T - nch) return;
+  // workgroup holding chunk x: the last w with floor(w T / nwg) <= x
+  auto owner = [&](int x) { return static_cast<int>((static_cast<long long>(x + 1) * P.nwg + T - 1) / T) - 1; };
+  const int w0 = max(0, owner(A)), w1 = min(P.nwg - 1, owner(A + nch - 1));
+  if (w0 >= w1) return;  // finished by that workgroup
+  const bool w0_late = static_cast<long long>(w0) * T / P.nwg < A;
+  const bool sparse = T < P.nwg;  // else every workgroup's range holds a chunk
+  const int rr = r - rg * P.rows_per_wg;
   float M = -INFINITY, wsum = 0.f;
   f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;
-  for (int s0 = 0; s0 < ns; s0 += U) {
+  constexpr int U = 8;
+  for (int w = w0; w <= w1; w += U) {
     float ms[U], ls[U];
     f32x4 os[U];
+    bool use[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const size_t slot = base + static_cast<size_t>(min(s0 + u, ns - 1)) * P.rows_cap;
-      ms[u] = P.ws_ml[slot * 2];
-      ls[u] = P.ws_ml[slot * 2 + 1];
-      os[u] = *reinterpret_cast<const f32x4 *>(P.ws_o + slot * D + c);
+      const int wu = min(w + u, w1);
+      const int slot = 2 * wu + ((wu == w0 && w0_late) ? 1 : 0);
+      const size_t srow = static_cast<size_t>(slot) * P.slot_rows + rr;
+      // with fewer chunks than workgroups some ranges are empty: those
+      // workgroups wrote nothing
+      use[u] = w + u <= w1 &&
+               (!sparse || static_cast<long long>(wu) * T / P.nwg < static_cast<long long>(wu + 1) * T / P.nwg);
+      ms[u] = P.ws_ml[srow * 2];
+      ls[u] = P.ws_ml[srow * 2 + 1];
+      os[u] = *reinterpret_cast<const f32x4 *>(P.ws_o + srow * D + c);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (s0 + u >= ns || ms[u] == -INFINITY) continue;
+      if (!use[u] || ms[u] == -INFINITY) continue;
       const float Mn = fmaxf(M, ms[u]);
-      const float a = exp2f(M - Mn);   // 0 when M was -inf
-      const float w = exp2f(ms[u] - Mn);
-      wsum = wsum * a + w * ls[u];
-      o = o * a + os[u] * w;
+      const float a = exp2f(M - Mn);  // 0 when M was -inf
+      const float wt = exp2f(ms[u] - Mn);
+      wsum = wsum * a + wt * ls[u];
+      o = o * a + os[u] * wt;
       M = Mn;
     }
   }
@@ -534,7 +748,8 @@ __global__ __launch_bounds__(256) void tree_attn_merge_kernel(Params P) {
 }
 
 struct Plan {
-  int rbw, row_groups, rows_per_wg, rows_cap, split_len, nsplit;
+  int rbw, row_groups, rows_per_wg, rows_cap, slot_rows, nwg;
+  long long chunks;  // chunks of the largest batch the bounds allow
   size_t ws_bytes;
 };
 
@@ -543,33 +758,40 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int max_n) {
   const int G = Hq / Hkv;
   const int rows = max_n * G;
   const int rb = (rows + 15) / 16;
-  const long long L = static_cast<long long>(max_ctx) + max_n;
   // Row blocks per wavefront.  With few (request, KV head) units a
-  // workgroup's time is latency-bound and more, lighter workgroups win
-  // (measured), so one row block per wave is used as long as that makes at
-  // most two row groups (each group re-reads the K/V tiles).  Otherwise the
-  // fewest row groups (at most 3 row blocks per wave: 4 spill at d = 128).
+  // workgroup's time is dominated by its fixed costs (first loads, partial
+  // write) and lighter workgroups win (measured: 240 rows of one request at
+  // 4K context, 28 us with one block per wave in two row groups against 36
+  // with two), so one block per wave is used while that makes at most two
+  // row groups and fewer than 256 units; otherwise the fewest row groups
+  // (each re-reads the unit's K/V), up to 3 blocks per wave (4 spill at
+  // d = 128).
   const int rg1 = (rows + kWaves * 16 - 1) / (kWaves * 16);
   if (rg1 <= 2 && static_cast<long long>(B) * Hkv * rg1 < 256) p.rbw = 1;
-  else if (rb <= kWaves) p.rbw = 1;
-  else if (rb <= 2 * kWaves) p.rbw = 2;
-  else p.rbw = 3;
+  else p.rbw = rb <= kWaves ? 1 : rb <= 2 * kWaves ? 2 : 3;
   p.rows_per_wg = kWaves * p.rbw * 16;
   p.row_groups = (rows + p.rows_per_wg - 1) / p.rows_per_wg;
   p.rows_cap = rb * 16;
-  // split the keys so that about 256 workgroups (one per CU) run at once
-  // (128 and 512 measured slower, and so did a 2-stage ring with two
-  // workgroups per CU for long key ranges)
+  p.slot_rows = p.rows_cap < p.rows_per_wg ? p.rows_cap : p.rows_per_wg;
+  const long long L = static_cast<long long>(max_ctx) + max_n;
+  p.chunks = static_cast<long long>(B) * Hkv * p.row_groups * ((L + KCH - 1) / KCH);
+  // one workgroup per CU, each taking at least MIN_CHUNKS chunks.  With at
+  // most half as many units as CUs the count is a multiple of the units, so
+  // that when every request has the bounds' lengths (one request, or a
+  // uniform batch) each range lies inside one unit and leaves one partial.
   const long long units = static_cast<long long>(B) * Hkv * p.row_groups;
-  const long long target = 256;
-  long long want = units > 0 ? (target + units - 1) / units : 1;
-  if (want < 1) want = 1;
-  long long len = (L + want - 1) / want;
-  len = (len + KCH - 1) / KCH * KCH;  // whole chunks: a partial last chunk costs a whole one
-  if (len < MIN_SPLIT) len = MIN_SPLIT;
-  p.split_len = static_cast<int>(len);
-  p.nsplit = static_cast<int>((L + len - 1) / len);
-  p.ws_bytes = p.nsplit > 1 ? static_cast<size_t>(B) * Hkv * p.nsplit * p.rows_cap * (d + 2) * sizeof(float) : 0;
+  const long long nch = (L + KCH - 1) / KCH;
+  long long nwg;
+  if (units * 2 <= kMaxWorkgroups) {
+    long long per = kMaxWorkgroups / units;
+    if (per > nch / MIN_CHUNKS) per = nch / MIN_CHUNKS;
+    nwg = units * (per < 1 ? 1 : per);
+  } else {
+    nwg = (p.chunks + MIN_CHUNKS - 1) / MIN_CHUNKS;
+  }
+  p.nwg = static_cast<int>(nwg < 1 ? 1 : nwg > kMaxWorkgroups ? kMaxWorkgroups : nwg);
+  p.ws_bytes = static_cast<size_t>(2) * p.nwg * p.slot_rows * (d + 2) * sizeof(float) +
+               (static_cast<size_t>(B) + 1) * sizeof(int32_t);
   return p;
 }
 
@@ -579,14 +801,15 @@ bool shape_ok(int B, int Hq, int Hkv, int d, int max_ctx, int max_n) {
 }
 
 template <int D>
-void launch(const Plan &pl, const Params &P, dim3 grid, hipStream_t s) {
+void launch(const Plan &pl, const Params &P, hipStream_t s) {
+  const dim3 grid(pl.nwg);
   if (pl.rbw == 1)
     hipLaunchKernelGGL((tree_attn_kernel<D, 1>), grid, dim3(kThreads), 0, s, P);
   else if (pl.rbw == 2)
     hipLaunchKernelGGL((tree_attn_kernel<D, 2>), grid, dim3(kThreads), 0, s, P);
   else
     hipLaunchKernelGGL((tree_attn_kernel<D, 3>), grid, dim3(kThreads), 0, s, P);
-  if (pl.nsplit > 1) {
+  if (pl.nwg > 1) {
     constexpr int RPB = 256 / (D / 4);
     dim3 mg((pl.rows_cap + RPB - 1) / RPB, P.Hkv, P.B);
     hipLaunchKernelGGL(tree_attn_merge_kernel<D>, mg, dim3(256), 0, s, P);
@@ -613,6 +836,12 @@ extern "C" int graft_tree_attention(int B, int Hq, int Hkv, int d, float scale, 
                 max_n);
   }
   if (B == 0) return GRAFT_OK;
+  if (B > GRAFT_ATTN_MAX_BATCH)
+    return fail(GRAFT_EINVAL, "tree_attention: B=%d > %d", B, GRAFT_ATTN_MAX_BATCH);
+  const Plan pl = make_plan(B, Hq, Hkv, d, max_ctx, max_n);
+  if (pl.chunks > INT32_MAX || Hkv > 65535)
+    return fail(GRAFT_EINVAL, "tree_attention: %lld key chunks (B * Hkv * row groups * ceil((max_ctx + max_n) / 64)) "
+                              "exceed 2^31 - 1", pl.chunks);
   if (!q || !kcache || !vcache || !kv_off || !ctx_len || !n || !row_off || !mask || !out)
     return fail(GRAFT_EINVAL, "tree_attention: NULL array");
   if (!graft::aligned16(q) || !graft::aligned16(kcache) || !graft::aligned16(vcache) || !graft::aligned16(out) ||
@@ -622,13 +851,10 @@ extern "C" int graft_tree_attention(int B, int Hq, int Hkv, int d, float scale, 
   if (kv_head_stride < static_cast<int64_t>(max_ctx + max_n) * d)
     return fail(GRAFT_EINVAL, "tree_attention: kv_head_stride %lld < (max_ctx + max_n) * d",
                 static_cast<long long>(kv_head_stride));
-  const Plan pl = make_plan(B, Hq, Hkv, d, max_ctx, max_n);
-  if (ws_bytes < pl.ws_bytes || (pl.ws_bytes > 0 && !ws))
+  if (ws_bytes < pl.ws_bytes || !ws)
     return fail(GRAFT_EINVAL, "tree_attention: workspace %zu bytes < %zu", ws_bytes, pl.ws_bytes);
-  if (pl.ws_bytes > 0 && !graft::aligned16(ws))  // partial O rows are moved 16 bytes at a time
+  if (!graft::aligned16(ws))  // partial O rows are moved 16 bytes at a time
     return fail(GRAFT_EINVAL, "tree_attention: workspace must be 16-byte aligned");
-  if (pl.nsplit > 65535 || static_cast<long long>(Hkv) * pl.row_groups > 65535 || B > 65535)
-    return fail(GRAFT_EINVAL, "tree_attention: grid too large");
   graft::clear_error();
   Params P{};
   P.B = B;
@@ -647,19 +873,19 @@ extern "C" int graft_tree_attention(int B, int Hq, int Hkv, int d, float scale, 
   P.max_n = max_n;
   P.row_off = row_off;
   P.mask = mask;
-  P.split_len = pl.split_len;
-  P.nsplit = pl.nsplit;
+  P.nwg = pl.nwg;
   P.rows_per_wg = pl.rows_per_wg;
   P.row_groups = pl.row_groups;
-  P.rows_cap = pl.rows_cap;
+  P.slot_rows = pl.slot_rows;
   P.out = out;
   P.lse = lse;
+  const size_t slots = static_cast<size_t>(2) * pl.nwg * pl.slot_rows;
   P.ws_o = static_cast<float *>(ws);
-  P.ws_ml = pl.ws_bytes ? P.ws_o + static_cast<size_t>(B) * Hkv * pl.nsplit * pl.rows_cap * d : nullptr;
+  P.ws_ml = P.ws_o + slots * d;
+  P.ws_pre = reinterpret_cast<int32_t *>(P.ws_ml + slots * 2);
   P.err = err_flag;
-  dim3 grid(pl.nsplit, Hkv * pl.row_groups, B);
   hipStream_t s = graft::as_stream(stream);
-  if (d == 128) launch<128>(pl, P, grid, s);
-  else launch<64>(pl, P, grid, s);
+  if (d == 128) launch<128>(pl, P, s);
+  else launch<64>(pl, P, s);
   return graft::check_launch("tree_attention");
 }

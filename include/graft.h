@@ -77,6 +77,7 @@ typedef void *graft_stream;
 #define GRAFT_MAX_UPDATE_ROWS 4096
 #define GRAFT_MAX_TEMPLATE_ROWS 4096
 #define GRAFT_MAX_BATCH 1024 /* requests per table update / retrieval call */
+#define GRAFT_ATTN_MAX_BATCH 8192 /* requests per tree attention call */
 
 /* return status */
 #define GRAFT_OK 0
@@ -283,13 +284,20 @@ int graft_tail_cut(int B, int L, const int32_t *root_token, const int32_t *block
  * kcache, vcache (device) bf16: slot s of kv head h of request b at
  *   element kv_off[b] + h * kv_head_stride + s * d; tree node j's key and
  *   value sit at slot ctx_len[b] + j.
- * ctx_len, n (device int32 [B]); max_ctx, max_n (host) bound them (grid
- *   sizing); a request above a bound is skipped with ERR_CAPACITY.
+ * ctx_len, n (device int32 [B]); max_ctx, max_n (host) bound them (work
+ *   and workspace sizing); a request above a bound is skipped with
+ *   ERR_CAPACITY.  B <= GRAFT_ATTN_MAX_BATCH, and the key chunks
+ *   B * Hkv * ceil(max_n * (Hq / Hkv) / rows per workgroup) *
+ *   ceil((max_ctx + max_n) / 64) must stay below 2^31, else GRAFT_EINVAL.
  * lse (device fp32 [rows, Hq], natural log) may be NULL.
  * d in {64, 128}; Hq % Hkv == 0; Hq / Hkv <= 16.
- * ws (device) holds split-K partials: at least
- *   graft_tree_attention_workspace_bytes(...) bytes (may be 0 -> ws NULL).
+ * ws (device, 16-byte aligned) holds the split partials and the requests'
+ *   chunk offsets: at least graft_tree_attention_workspace_bytes(...) bytes
+ *   (> 0 for B > 0; its contents need no clearing).
  * Output is bf16 rounded to nearest even; softmax and accumulation fp32.
+ * The key ranges are dealt over the workgroups by the batch's total work,
+ * so where a request's keys are split (and so its rounding) depends on the
+ * whole batch; a call is deterministic for given inputs.
  */
 size_t graft_tree_attention_workspace_bytes(int B, int Hq, int Hkv, int d, int max_ctx, int max_n);
 int graft_tree_attention(int B, int Hq, int Hkv, int d, float scale,

@@ -89,6 +89,11 @@ def test_host_argument_validation_launches_nothing(native):
     assert L.graft_tree_attention(1, 8, 2, 96, 0.1, *args) == U
     assert L.graft_tree_attention(1, 8, 3, 128, 0.1, *args) == E
     assert L.graft_tree_attention(0, 8, 2, 128, 0.1, *args) == 0
+    assert L.graft_tree_attention(8193, 8, 2, 128, 0.1, *args) == E  # above GRAFT_ATTN_MAX_BATCH
+    assert b"B=8193" in L.graft_last_error()
+    big = args[:6] + [1 << 30] + args[7:]  # 2^24 chunks per unit: 2^31 over 64 requests x 2 KV heads
+    assert L.graft_tree_attention(64, 8, 2, 128, 0.1, *big) == E
+    assert b"key chunks" in L.graft_last_error()
     # build tree
     bt = [1] * 24
     assert L.graft_build_tree(1, 7, *bt[:4], 10, *bt[:6], 100, 8, 0.0, *bt[:11]) == E
@@ -143,9 +148,37 @@ def test_workspace_sizes(native):
             # sampling: 64-row m tiles at every M, k keys plus one draw key per list
             T64 = -(-M // 64)
             assert L.graft_lmhead_sample_workspace_bytes(M, 151936, k) == M * streams(T64) * (k + 1) * 8, (M, k)
-    # tiny single-split attention needs no workspace; long context does
-    assert L.graft_tree_attention_workspace_bytes(1, 4, 2, 64, 100, 15) == 0
-    assert L.graft_tree_attention_workspace_bytes(1, 32, 8, 128, 32768, 63) > 0
+    # tree attention: two partial slots per workgroup (rows of one row group
+    # by d + 2 floats) and B + 1 chunk offsets.  One row block of 16 rows per
+    # wave while that keeps <= 2 row groups and < 256 units, else the fewest
+    # groups; workgroups: a multiple of the units while there are <= 128 of
+    # them (each taking >= 2 chunks), else one per two chunks of the largest
+    # batch the bounds allow, at most 256
+    def attn_ws(B, Hq, Hkv, d, max_ctx, max_n):
+        rows = max_n * (Hq // Hkv)
+        rb = -(-rows // 16)
+        rg1 = -(-rows // 128)
+        rbw = 1 if (rg1 <= 2 and B * Hkv * rg1 < 256) else (1 if rb <= 8 else 2 if rb <= 16 else 3)
+        per_wg = 128 * rbw
+        groups = -(-rows // per_wg)
+        nch = -(-(max_ctx + max_n) // 64)
+        units = B * Hkv * groups
+        if 2 * units <= 256:
+            nwg = units * max(1, min(256 // units, nch // 2))
+        else:
+            nwg = -(-(units * nch) // 2)
+        nwg = max(1, min(256, nwg))
+        return 2 * nwg * min(rb * 16, per_wg) * (d + 2) * 4 + (B + 1) * 4
+
+    for shape in ((1, 4, 2, 64, 100, 15), (1, 32, 8, 128, 32768, 63), (16, 32, 8, 128, 16384, 60),
+                  (3, 64, 8, 128, 7000, 64), (41, 4, 2, 64, 3000, 64), (1, 4, 2, 64, 0, 1)):
+        assert L.graft_tree_attention_workspace_bytes(*shape) == attn_ws(*shape), shape
+    # worked by hand: 30 rows, 2 units of 2 chunks, one workgroup each
+    assert attn_ws(1, 4, 2, 64, 100, 15) == 2 * 2 * 32 * 66 * 4 + 8
+    # one request at 4K context, 240 rows: 2 row groups of 128 x 8 KV heads
+    # = 16 units of 65 chunks, 16 workgroups each
+    assert attn_ws(1, 32, 8, 128, 4096, 60) == 2 * 256 * 128 * 130 * 4 + 8
+    assert L.graft_tree_attention_workspace_bytes(0, 32, 8, 128, 4096, 60) == 0
 
 
 def test_kv_compact_host_validation_launches_nothing(native):
@@ -241,11 +274,11 @@ def test_misaligned_arrays_are_rejected_before_any_launch(native):
     assert L.graft_lmhead_pack(100, 256, A, X, None) == E
     for h, w, g in ((X, A, A), (A, X, A), (A, A, X)):
         assert L.graft_lmhead_topk_sample(4, 256, 100, 4, 1.0, h, w, g, A, A, A, A, ws, None) == E
-    # tree attention: q, kcache, vcache, out, the split workspace, and the head stride
+    # tree attention: q, kcache, vcache, out, the workspace, and the head stride
     def att(q=A, k=A, v=A, out=A, wsp=A, stride=4096 * 128):
         return L.graft_tree_attention(1, 8, 2, 128, 0.1, q, k, v, A, stride, A, 4000, A, 60, A, A, out, None,
                                       wsp, ws, A, None)
-    assert L.graft_tree_attention_workspace_bytes(1, 8, 2, 128, 4000, 60) > 0  # split, so the workspace is used
+    assert L.graft_tree_attention_workspace_bytes(1, 8, 2, 128, 4000, 60) > 0
     for kw in ({"q": X}, {"k": X}, {"v": X}, {"out": X}, {"wsp": X}, {"stride": 4096 * 128 + 4}):
         assert att(**kw) == E, kw
     # KV compaction: caches and the layer stride
