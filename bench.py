@@ -359,6 +359,47 @@ def measure(cfg, steps, warmup, with_cpu, extras):
     return rep, cpu
 
 
+def topk_probe(M=960, V=151936, reps=8):
+    """The top-k on materialised logits (A5 off the round's path): one
+    graft_lmhead_topk call with the logits given, on seeded N(0, 1) fp32
+    logits of the batched workload's shape, cold: a read of 1 GiB of other
+    memory (no writes, so no dirty lines to write back) before every call.
+    A plain reduction over the same logits (torch.amax, row maxima) timed
+    the same way is the streaming reference."""
+    import torch
+    from draft_tree_verification_parent_amd import api
+
+    g = torch.Generator(device="cuda").manual_seed(5)
+    logits = torch.randn(M, V, device="cuda", generator=g)
+    evict = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    out = {"workload": f"top-k of {M} x {V} fp32 logits, cold", "bytes": M * V * 4}
+    for k in (8, 16):
+        ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+        vals = torch.empty(M, k, dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(api.graft_lmhead_topk_workspace_bytes(M, V, k), 16), dtype=torch.uint8, device="cuda")
+
+        def timed(fn):
+            best = float("inf")
+            for _ in range(reps):
+                torch.amax(evict)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                best = min(best, e0.elapsed_time(e1) * 1e3)
+            return best
+
+        us = timed(lambda: api.graft_lmhead_topk(M, 0, V, k, None, None, logits, ids, vals, ws))
+        ref = torch.topk(logits, k, dim=1)
+        out[f"k{k}"] = {"us": round(us, 1), "GB/s": round(M * V * 4 / us / 1e3, 1),
+                        "hbm_frac": round(M * V * 4 / us / 1e3 / HBM_PEAK_GBS, 4),
+                        "values_match_torch_topk": bool(torch.equal(vals, ref.values))}
+    ref_us = timed(lambda: torch.amax(logits, dim=1))
+    out["torch_amax_us"] = round(ref_us, 1)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,6 +410,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--topk-probe", action="store_true",
+                    help="only time the top-k of materialised logits (960 x 151936 fp32, cold)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -391,6 +434,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n * 4, "launches": 5}))
+        return
+
+    if args.topk_probe:
+        print(json.dumps(topk_probe()))
         return
 
     head, cpu = measure(args.cfg, args.steps, args.warmup, not args.no_cpu_baseline, extras=False)

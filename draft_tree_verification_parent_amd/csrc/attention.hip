@@ -306,18 +306,15 @@ __device__ __forceinline__ void attend_segment(const Params &P, unsigned char *s
   const int kfrag = l16 * TL::ROW;
   const int vfrag = vr * TL::ROW + 8 * ((vcol >> 2) & 1);
 
-  // One chunk: S^T for its 64 keys, one online-softmax update per row
-  // block, then O^T += V^T . P^T over its two 32-key halves.  NA, the
-  // number of active row blocks (always the first NA), is a compile-time
-  // constant so the MFMAs carry no branches and the fragment reads can be
-  // issued ahead of them.
-  auto compute = [&](auto na_tag, int c) {
+  // A chunk's work in three phases: S^T for its 64 keys (MFMA), one
+  // online-softmax update per row block (VALU), then O^T += V^T . P^T over
+  // its two 32-key halves (MFMA).  NA, the number of active row blocks
+  // (always the first NA), is a compile-time constant so the MFMAs carry no
+  // branches and the fragment reads can be issued ahead of them.
+  auto s_phase = [&](auto na_tag, int c, f32x4(&sacc)[RBW][4]) {
     constexpr int NA = decltype(na_tag)::value;
     const lds_u8 *ks = (const lds_u8 *)sm + (c % NS) * TL::SB;
-    const lds_u8 *vs = ks + TL::KB;
-    const int c0 = k_begin + c * KCH;
     // S^T blocks: sacc[j][kb][i] = S[row l16][key c0 + kb*16 + 4g + i]
-    f32x4 sacc[RBW][4];
 #pragma unroll
     for (int j = 0; j < NA; ++j)
 #pragma unroll
@@ -355,10 +352,13 @@ __device__ __forceinline__ void attend_segment(const Params &P, unsigned char *s
         }
       }
     }
+  };
+  auto x_phase = [&](auto na_tag, int c, const f32x4(&sacc)[RBW][4], bf16x8(&pb)[RBW][2]) {
+    constexpr int NA = decltype(na_tag)::value;
+    const int c0 = k_begin + c * KCH;
     // online softmax (base 2).  A chunk that lies entirely inside the
     // context needs no mask (uniform test).
     const bool unmasked = c0 + KCH <= ctx && c0 + KCH <= k_end;
-    bf16x8 pb[RBW][2];  // P^T operand of each 32-key half
 #pragma unroll
     for (int j = 0; j < NA; ++j) {
       // raw scores; the scale is folded into the exp2 argument below
@@ -412,6 +412,10 @@ __device__ __forceinline__ void attend_segment(const Params &P, unsigned char *s
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[j][t][e] = static_cast<__bf16>(x[8 * t + e]);
     }
+  };
+  auto o_phase = [&](auto na_tag, int c, const bf16x8(&pb)[RBW][2]) {
+    constexpr int NA = decltype(na_tag)::value;
+    const lds_u8 *vs = (const lds_u8 *)sm + (c % NS) * TL::SB + TL::KB;
     // O^T += V^T . P^T: lane (d = db*16 + l16, g) needs keys {4g..4g+3}
     // and {16+4g..16+4g+3} of the half for head-dim column d; the 16-lane
     // transpose read delivers them when lane a of the group points at key
@@ -437,9 +441,12 @@ __device__ __forceinline__ void attend_segment(const Params &P, unsigned char *s
 
   // ---- ring: chunks c+1 .. c+NS-2 stay in flight while chunk c is computed.
   // A wave without active row blocks still issues its share of every
-  // chunk's DMAs and meets the others at each barrier.
+  // chunk's DMAs and meets the others at each barrier.  (Running the two
+  // waves of each SIMD half a chunk apart, one in its softmax while the
+  // other runs its products, measured no faster.)
   constexpr int PER = 2 * DI;  // DMAs per wave per chunk
   auto run = [&](auto na_tag) {
+    constexpr int NA = decltype(na_tag)::value;
     for (int c = 0; c < nch; ++c) {
       static_assert(NS - 2 <= 2, "the waits below cover at most two younger chunks");
       const int younger = min(nch - 1 - c, NS - 2);  // chunks issued after c
@@ -447,7 +454,13 @@ __device__ __forceinline__ void attend_segment(const Params &P, unsigned char *s
       else if (younger == 1) ring_barrier<PER>();
       else ring_barrier<0>();
       if (c + NS - 1 < nch) issue(c + NS - 1);  // into the stage chunk c - 1 used
-      if constexpr (decltype(na_tag)::value > 0) compute(na_tag, c);
+      if constexpr (NA > 0) {
+        f32x4 sacc[RBW][4];  // S^T of the chunk
+        bf16x8 pb[RBW][2];   // P^T operand of each 32-key half
+        s_phase(na_tag, c, sacc);
+        x_phase(na_tag, c, sacc, pb);
+        o_phase(na_tag, c, pb);
+      }
     }
   };
   int nact = 0;  // active row blocks are the first nact (wave-uniform)

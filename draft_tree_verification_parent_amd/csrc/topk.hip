@@ -7,12 +7,14 @@
 //
 // Two passes, both bound by the read of the logits:
 //  1. grid (slices, rows): each thread keeps a sorted top-K list in
-//     registers over its strided part of a slice (coalesced float4 reads,
-//     filtered by a wave-wide bound so that few entries are inserted),
+//     registers over its strided part of a slice (coalesced float4 reads;
+//     a batch runs inserts only when its largest entry passes a wave-wide
+//     bound, so that after the first batches almost none does),
 //     each wavefront merges its 64 lists with k rounds of a (value, id)
 //     butterfly max, and wave 0 merges the four wave results; k candidates
 //     per (row, slice) go to the workspace.
-//  2. one workgroup per row merges the slices' candidates the same way.
+//  2. one workgroup per row merges the slices' candidates the same way
+//     (not needed with one slice per row, the case past 256 rows).
 // The (value desc, id asc) order is total on non-NaN values, so the result
 // does not depend on how the vocabulary is split.
 #include <climits>
@@ -24,7 +26,7 @@
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSliceQuantum = 1024;  // 256 threads x float4
+constexpr int kSliceQuantum = 4;  // slices start on 16-byte boundaries
 
 using graft::TopKeys;
 
@@ -54,43 +56,72 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
   // 16 slots rarely run an insert.  (A uniform trip count keeps all 64 lanes
   // in the cross-lane max.)
   uint32_t bound = 0;
-  constexpr int U = 4;  // 16-byte loads per thread per batch, issued together
+  // 16-byte loads per thread per batch, issued together (the longer lists'
+  // larger per-batch bound update is spread over twice the entries)
+  constexpr int U = K <= 8 ? 4 : 8;
   if ((V & 3) == 0) {
-    for (int base = lo; base < hi; base += kThreads * 4 * U) {
+    // Whole batches need no bounds checks.  The screen is a float compare
+    // against the bound's value, !(x < bf): for numbers it is order(x) >=
+    // bound; while the bound is 0 (no lane full yet) bf is a NaN and every
+    // entry passes; a NaN entry passes too, and the list's own key compare
+    // then keeps it out unless the list has room (NaN ranks last).  A batch
+    // runs its inserts, and the bound is raised, only when the wave's
+    // largest entry passes, which after the first batches is rare.
+    constexpr int B = kThreads * 4 * U;
+    int base = lo;
+    float bf = __uint_as_float(0xFFFFFFFFu);  // the value of order 0: a NaN
+    for (; base + B <= hi; base += B) {
       float4 x[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = base + (u * kThreads + tid) * 4;
-        x[u] = c < hi ? *reinterpret_cast<const float4 *>(row + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      for (int u = 0; u < U; ++u) x[u] = *reinterpret_cast<const float4 *>(row + base + (u * kThreads + tid) * 4);
       if (base == lo) {
         // first batch (uniform): the K-th largest of the 64 lane maxima, so
         // the first inserts are already filtered
         uint32_t lm = 0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int c = base + (u * kThreads + tid) * 4;
           const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const uint32_t o = c + e < hi ? graft::float_order(xs[e]) : 0u;
+            const uint32_t o = graft::float_order(xs[e]);
             lm = o > lm ? o : lm;
           }
         }
         bound = graft::wave_kth_u32<K>(lm);
+        bf = graft::key_value(static_cast<uint64_t>(bound) << 32);
       }
+      float mx = fmaxf(fmaxf(x[0].x, x[0].y), fmaxf(x[0].z, x[0].w));
+#pragma unroll
+      for (int u = 1; u < U; ++u) mx = fmaxf(mx, fmaxf(fmaxf(x[u].x, x[u].y), fmaxf(x[u].z, x[u].w)));
+      // (fmaxf drops NaNs unless all are: a batch whose numbers all fail
+      // skips its NaNs, which rank below them)
+      if (__builtin_amdgcn_ballot_w64(!(mx < bf)) == 0) continue;  // uniform
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = base + (u * kThreads + tid) * 4;
         const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (c + e < hi && graft::float_order(xs[e]) >= bound) L.insert(graft::rank_key(xs[e], c + e));
+          if (!(xs[e] < bf)) L.insert(graft::rank_key(xs[e], c + e));
       }
       // each lane's list head is its largest entry: K lanes hold an entry
       // at least the K-th largest head
       const uint32_t lb = graft::wave_kth_u32<K>(static_cast<uint32_t>(L.k[0] >> 32));
-      bound = lb > bound ? lb : bound;
+      if (lb > bound) {
+        bound = lb;
+        bf = graft::key_value(static_cast<uint64_t>(bound) << 32);
+      }
+    }
+    // the partial batch at the end of the slice, entry by entry
+    for (; base < hi; base += kThreads * 4) {
+      const int c = base + tid * 4;
+      if (c < hi) {
+        const float4 v = *reinterpret_cast<const float4 *>(row + c);
+        const float xs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < hi && graft::float_order(xs[e]) >= bound) L.insert(graft::rank_key(xs[e], c + e));
+      }
     }
   } else {
     for (int base = lo; base < hi; base += kThreads * U) {
@@ -245,10 +276,16 @@ namespace graft {
 
 TopkPlan topk_plan(int M, int V, int k) {
   TopkPlan p;
-  const int max_slices = (V + kSliceQuantum - 1) / kSliceQuantum;
-  int want = M > 0 ? (1024 + M - 1) / M : 1;
-  if (want < 1) want = 1;
+  // at least one workgroup per CU, slices of equal length (at least 4096
+  // entries: a slice's first batch sets its bound).  Past 256 rows one
+  // workgroup per row: more slices measured slower (960 x 151936 fp32
+  // logits, cold: 110 us with one slice per row, 119 with two, 121 with
+  // four; k = 16: 141, 174, 222), each adding its own bound set-up, list
+  // extraction and merge.
+  const int max_slices = (V + 4095) / 4096;
+  int want = M > 0 ? (256 + M - 1) / M : 1;
   if (want > max_slices) want = max_slices;
+  if (want < 1) want = 1;
   int per = (V + want - 1) / want;
   per = (per + kSliceQuantum - 1) / kSliceQuantum * kSliceQuantum;
   p.slice_len = per;
