@@ -181,30 +181,35 @@ def test_attention_long_context_concentrated(cfg):
         f"largest row-scaled err {worst_ratio:.3g}")
 
 
-def test_end_to_end_argmax_where_margin_is_clear():
+@pytest.mark.parametrize("cfg,n_rows", [(2, 60), (4, 60), (5, 64)])
+def test_end_to_end_argmax_where_margin_is_clear(cfg, n_rows):
     """Rows whose fp64 top-1/top-2 logit margin is far above the lm-head's
-    error take the same argmax on the GPU as in the oracle (cfg 2)."""
+    error take the same argmax on the GPU as in the oracle, with no
+    stage-by-stage handoff: the round as the bench runs it (fused lm-head +
+    top-k; for the 960-row batch the 256 x 256 tiles), rows spread over
+    every request."""
     _need_gpu()
-    wl, ri, w, ts, hidden, vr = run_gpu_round(2)
+    wl, ri, w, ts, hidden, vr = run_gpu_round(cfg, fused=True)
     gpu_arg = vr.topk_id.cpu().numpy()[:, 0]
-    rows = np.arange(8)
+    n_all = hidden.shape[0]
+    rows = np.unique(np.linspace(0, n_all - 1, min(n_rows, n_all)).astype(np.int64))
     best = np.full(len(rows), -np.inf)
     second = np.full(len(rows), -np.inf)
     arg = np.zeros(len(rows), np.int64)
     for c0 in range(0, ri.V, 16384):
         lg = OL.logits(hidden[rows], w[c0:c0 + 16384]).astype(np.float64)
+        top2 = np.argsort(-lg, axis=1, kind="stable")[:, :2]
         for j in range(len(rows)):
-            o = np.argsort(-lg[j], kind="stable")[:2]
-            for idx in o:
+            for idx in top2[j]:
                 v = lg[j, idx]
                 if v > best[j]:
                     second[j], best[j], arg[j] = best[j], v, c0 + idx
                 elif v > second[j]:
                     second[j] = v
     clear = (best - second) > 1e-3
-    assert clear.sum() >= 4
+    assert clear.sum() >= len(rows) // 2
     assert np.array_equal(gpu_arg[rows][clear], arg[clear])
-    say(f"[e2e] {int(clear.sum())} of {len(rows)} rows have a clear margin; all match")
+    say(f"[e2e] cfg {cfg}: {int(clear.sum())} of {len(rows)} rows have a clear margin; all match")
 
 
 @pytest.mark.parametrize("cfg,per_graph", [(1, 1), (2, 1), (2, 3)])
