@@ -42,10 +42,12 @@ SIGNATURES = {
     "graft_kv_compact": (c_int, [c_int, c_int, c_int, c_int, P, P, c_int64, P, c_int64, P, P, P, P, P, P, P, P,
                                  P]),
     "graft_make_template": (c_int, [c_int, c_int, c_int, P, P]),
+    "graft_table_save": (c_int, [c_char_p, c_int, c_int, P, P]),
+    "graft_table_load": (c_int, [c_char_p, c_int, c_int, P, P]),
     "graft_stage_budget": (c_int, [c_int, P, P]),
 }
 
-GRAFT_OK, GRAFT_EINVAL, GRAFT_EUNSUPPORTED, GRAFT_EHIP = 0, -1, -2, -3
+GRAFT_OK, GRAFT_EINVAL, GRAFT_EUNSUPPORTED, GRAFT_EHIP, GRAFT_EIO = 0, -1, -2, -3, -4
 ERR_TOKEN, ERR_PARENT, ERR_NOT_CLOSED, ERR_CAPACITY, ERR_RANK, ERR_ALIGN = 1, 2, 4, 8, 16, 32
 SRC_ROOT, SRC_DRAFT, SRC_RETRIEVED, SRC_REPLACED = 0, 1, 2, 3
 TREE_PRUNE, TREE_STATIC_REPLACE, TREE_TAIL = 0, 1, 2

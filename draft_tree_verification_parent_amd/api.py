@@ -2,9 +2,12 @@
 
 Argument marshalling only -- every step runs in libgraft's HIP kernels.
 Device tensors must be contiguous and on the current GPU; work is enqueued
-on `stream` (default: torch's current stream) and nothing synchronises.
+on `stream` (default: torch's current stream) and nothing synchronises,
+except the table checkpoint calls, which wait for their stream.
 """
 from __future__ import annotations
+
+import os
 
 import numpy as np
 import torch
@@ -51,6 +54,20 @@ def graft_table_update_retrieve(table, upd_n, upd_row_off, upd_rows, upd_token, 
                 _p(root_token, "i32", "root_token"), _p(tmpl_parent, "i32", "tmpl_parent"),
                 _p(tmpl_rank, "i32", "tmpl_rank"), _p(tmpl_off, "i32", "tmpl_off"), int(tmpl_rows),
                 _p(ret_token, "i32", "ret_token"), _p(err, "i32", "err"), _s(stream))
+
+
+def graft_table_save(path, table, stream=None):
+    """Writes the [V, k] int32 successor table (device) to `path`; waits for
+    the stream."""
+    V, k = table.shape
+    return call("graft_table_save", os.fsencode(path), int(V), int(k), _p(table, "i32", "table"), _s(stream))
+
+
+def graft_table_load(path, table, stream=None):
+    """Reads a table file into `table` (device, [V, k] int32, overwritten
+    only when the file checks out); waits for the stream."""
+    V, k = table.shape
+    return call("graft_table_load", os.fsencode(path), int(V), int(k), _p(table, "i32", "table"), _s(stream))
 
 
 def graft_build_tree(mode, cand_parent, cand_token, cand_score, cand_off, max_cand, budget,

@@ -16,10 +16,13 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgraft.so")
 
-SOURCES = ["common.cpp", "template.cpp", "table.hip", "build_tree.hip", "accept.hip",
+SOURCES = ["common.cpp", "template.cpp", "table_io.cpp", "table.hip", "build_tree.hip", "accept.hip",
            "topk.hip", "lmhead.hip", "attention.hip", "kv_compact.hip"]
 ARCH = "gfx950"
-CXXFLAGS = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
+# Warnings are errors, except clang's note that an inline-asm clobber names
+# the reserved register M0: the LDS-DMA statements write M0 themselves and say
+# so, and the compiler re-initialises M0 before each of its own uses.
+CXXFLAGS = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function", "-Werror", "-Wno-error=inline-asm",
             f"-I{INCLUDE}", f"-I{CSRC}"]
 # Packed-fp32 instructions are kept out of every kernel.
 HIPFLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -84,6 +84,7 @@ typedef void *graft_stream;
 #define GRAFT_EINVAL (-1)       /* bad argument / shape; nothing launched */
 #define GRAFT_EUNSUPPORTED (-2) /* valid but not built (e.g. head dim 96) */
 #define GRAFT_EHIP (-3)         /* a HIP launch failed */
+#define GRAFT_EIO (-4)          /* a file could not be opened, read or written */
 
 /* device error-flag bits */
 #define GRAFT_ERR_TOKEN 1      /* token or successor id outside [0, V) */
@@ -148,6 +149,25 @@ int graft_table_update_retrieve(int32_t *table, int V, int k,
                                 int B, const int32_t *root_token, const int32_t *tmpl_parent,
                                 const int32_t *tmpl_rank, const int32_t *tmpl_off, int tmpl_rows,
                                 int32_t *ret_token, int32_t *err_flag, graft_stream stream);
+
+/*
+ * Successor-table checkpoint.  The table is the only state a round leaves
+ * besides the KV cache, and a warmed table is kept across rounds (Graft
+ * page, section 6: warm-up fills the table, later rounds keep updating it).
+ * File: 32-byte header ("GRAFTTB1", V and k as little-endian int64, the
+ * 64-bit FNV-1a hash of the payload), then table [V, k] int32 row-major,
+ * little-endian.
+ * graft_table_save copies table (device) to the host on `stream`, waits for
+ * the stream, and writes the file under path + ".tmp", renamed to path when
+ * whole.  graft_table_load reads the file, checks the magic, V and k (which
+ * must equal the arguments), the length, the hash and that every entry lies
+ * in [0, V), and only then copies the rows to table (device) on `stream`
+ * and waits for it; on any error table is left untouched.
+ * 1 <= k <= GRAFT_MAX_K.  Errors: GRAFT_EINVAL (arguments, or a file that is
+ * not this table), GRAFT_EIO (open, read, write, rename), GRAFT_EHIP (copy).
+ */
+int graft_table_save(const char *path, int V, int k, const int32_t *table, graft_stream stream);
+int graft_table_load(const char *path, int V, int k, int32_t *table, graft_stream stream);
 
 /*
  * Tree construction and flattening for B requests.

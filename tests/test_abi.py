@@ -288,3 +288,68 @@ def test_misaligned_arrays_are_rejected_before_any_launch(native):
     assert kvc(k=X) == E
     assert kvc(v=X) == E
     assert kvc(layers=2, layer_stride=8 * 4096 * 128 + 4) == E
+
+
+# ----------------------------------------------------------------------------- table checkpoint files
+
+def _fnv1a64(data: bytes) -> int:
+    """FNV-1a, 64-bit, from its published definition (offset basis, prime)."""
+    h = 0xCBF29CE484222325
+    for b in data:
+        h ^= b
+        h = (h * 0x100000001B3) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def write_table_file(path, table, magic=b"GRAFTTB1", V=None, k=None, checksum=None, extra=b""):
+    """An independent writer of the table file format (header: magic, V, k,
+    FNV-1a of the payload; then int32 rows, little-endian)."""
+    t = np.ascontiguousarray(table, dtype="<i4")
+    payload = t.tobytes()
+    V = t.shape[0] if V is None else V
+    k = t.shape[1] if k is None else k
+    cs = _fnv1a64(payload) if checksum is None else checksum
+    with open(path, "wb") as f:
+        f.write(magic + int(V).to_bytes(8, "little") + int(k).to_bytes(8, "little") + int(cs).to_bytes(8, "little"))
+        f.write(payload + extra)
+
+
+def test_fnv1a64_matches_published_vectors():
+    # test vectors of the FNV-1a 64-bit definition
+    assert _fnv1a64(b"") == 0xCBF29CE484222325
+    assert _fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert _fnv1a64(b"foobar") == 0x85944171F73967E8
+
+
+def test_table_load_rejects_bad_files_before_any_copy(native, tmp_path):
+    """Every check of a table file runs on the host before the device copy:
+    the device pointer given here is never dereferenced."""
+    L = native.lib()
+    E, EIO = native.GRAFT_EINVAL, native.GRAFT_EIO
+    fake = 1 << 20
+    V, k = 50, 4
+    t = np.random.default_rng(3).integers(0, V, (V, k)).astype(np.int32)
+    p = str(tmp_path / "t.bin").encode()
+    assert L.graft_table_load(str(tmp_path / "missing.bin").encode(), V, k, fake, None) == EIO
+    write_table_file(p, t, magic=b"NOTTABLE")
+    assert L.graft_table_load(p, V, k, fake, None) == E and b"not a table file" in L.graft_last_error()
+    write_table_file(p, t)
+    assert L.graft_table_load(p, V + 1, k, fake, None) == E and b"50 x 4" in L.graft_last_error()
+    assert L.graft_table_load(p, V, k + 1, fake, None) == E
+    write_table_file(p, t, extra=b"\0")
+    assert L.graft_table_load(p, V, k, fake, None) == E and b"payload bytes" in L.graft_last_error()
+    write_table_file(p, t[:-1], V=V)
+    assert L.graft_table_load(p, V, k, fake, None) == E
+    write_table_file(p, t, checksum=_fnv1a64(t.tobytes()) ^ 1)
+    assert L.graft_table_load(p, V, k, fake, None) == E and b"checksum" in L.graft_last_error()
+    bad = t.copy()
+    bad[7, 2] = V  # a token id out of range, with a valid checksum
+    write_table_file(p, bad)
+    assert L.graft_table_load(p, V, k, fake, None) == E and b"entry 30" in L.graft_last_error()
+    # arguments
+    assert L.graft_table_load(None, V, k, fake, None) == E
+    assert L.graft_table_load(p, V, 0, fake, None) == E
+    assert L.graft_table_load(p, V, 17, fake, None) == E
+    assert L.graft_table_load(p, V, k, None, None) == E
+    assert L.graft_table_save(p, 0, k, fake, None) == E
+    assert L.graft_table_save(None, V, k, fake, None) == E

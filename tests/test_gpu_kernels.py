@@ -1277,3 +1277,35 @@ def test_attention_length_above_bound_is_flagged(api):
                              torch.full((4,), 1, dtype=torch.int64, device="cuda"), out, None, ws, err)
     torch.cuda.synchronize()
     assert err.item() & ERR_CAPACITY
+
+
+# ----------------------------------------------------------------------------- table checkpoint
+
+def test_table_save_load_round_trip(api, tmp_path):
+    """A table written by graft_table_save reads back bit for bit through an
+    independent reader of the file format and through graft_table_load; a
+    file with one flipped payload bit is refused and leaves the table as it
+    was."""
+    import test_abi as TA
+    V, k = 151936, 8
+    r = np.random.default_rng(17)
+    host = r.integers(0, V, (V, k)).astype(np.int32)
+    table = torch.from_numpy(host).cuda()
+    path = str(tmp_path / "table.bin")
+    assert api.graft_table_save(path, table) == 0
+    raw = open(path, "rb").read()
+    assert raw[:8] == b"GRAFTTB1"
+    assert int.from_bytes(raw[8:16], "little") == V and int.from_bytes(raw[16:24], "little") == k
+    assert int.from_bytes(raw[24:32], "little") == TA._fnv1a64(raw[32:])
+    assert np.array_equal(np.frombuffer(raw[32:], dtype="<i4").reshape(V, k), host)
+    other = torch.full((V, k), 3, dtype=torch.int32, device="cuda")
+    assert api.graft_table_load(path, other) == 0
+    assert torch.equal(other, table)
+    flipped = bytearray(raw)
+    flipped[32 + 4 * 12345] ^= 0x01
+    open(path, "wb").write(bytes(flipped))
+    before = other.clone()
+    from draft_tree_verification_parent_amd._native import GraftError
+    with pytest.raises(GraftError, match="checksum"):
+        api.graft_table_load(path, other)
+    assert torch.equal(other, before)
