@@ -569,8 +569,9 @@ __device__ inline void stream_start(const Params &P, int *s_pre, int *s_wsum, in
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       const int b = tid * PT + i;
-      if (b <= P.B) P.ws_pre[b] = s_pre[b];
+      if (b < P.B) P.ws_pre[b] = s_pre[b];
     }
+    if (tid == 0) P.ws_pre[P.B] = T;  // (b = B is past the owners' range when B = GRAFT_ATTN_MAX_BATCH)
   }
   const int s_w = static_cast<int>(static_cast<long long>(blockIdx.x) * T / P.nwg);
   // the request holding chunk s_w: s_pre[b] <= s_w < s_pre[b + 1] (one

@@ -1199,6 +1199,55 @@ def test_attention_concentrated_long_context(api, B, Hq, Hkv, d, ctxs, ns):
     say(f"[attention concentrated] max abs err {worst:.3g}")
 
 
+def test_attention_largest_batch(api):
+    """GRAFT_ATTN_MAX_BATCH requests, each with its own K/V capacity: the
+    first is long enough (40 chunks) to be split over two workgroups, whose
+    merge reads the chunk count the kernel stores after the batch's offsets;
+    8191 one-node requests with 0-3 context keys follow (every workgroup walks
+    about 32 of them)."""
+    B, Hq, Hkv, d = 8192, 2, 1, 64
+    r = np.random.default_rng(8192)
+    ctxs = [2540] + [int(c) for c in r.integers(0, 4, B - 1)]
+    ns = [20] + [1] * (B - 1)
+    caps = [(c + n + 7) // 8 * 8 for c, n in zip(ctxs, ns)]  # offsets stay multiples of 8 elements
+    kv_off = np.concatenate([[0], np.cumsum(caps)[:-1]]).astype(np.int64) * d
+    total = int(sum(caps))
+    row_off = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    rows = int(row_off[-1])
+    q = f32_to_bf16_bits(r.standard_normal((rows, Hq, d)).astype(np.float32))
+    kc = f32_to_bf16_bits(r.standard_normal((total, d)).astype(np.float32))
+    vc = f32_to_bf16_bits(r.standard_normal((total, d)).astype(np.float32))
+    mask = np.zeros(rows, np.uint64)
+    for i in range(ns[0]):  # request 0: a chain
+        mask[i] = (1 << (i + 1)) - 1
+    mask[ns[0]:] = 1
+    out = torch.zeros(rows, Hq, d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros(rows, Hq, dtype=torch.float32, device="cuda")
+    wsb = api.graft_tree_attention_workspace_bytes(B, Hq, Hkv, d, max(ctxs), max(ns))
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    err = err_buf()
+    scale = 1 / np.sqrt(d)
+    api.graft_tree_attention(Hq, Hkv, d, scale, dev_bf16(q), dev_bf16(kc.reshape(-1)), dev_bf16(vc.reshape(-1)),
+                             torch.from_numpy(kv_off).cuda(), (max(ctxs) + max(ns)) * d, dev_i32(ctxs), max(ctxs),
+                             dev_i32(ns), max(ns),
+                             dev_i32(row_off), torch.from_numpy(mask.view(np.int64)).cuda(), out, lse, ws, err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    got = out.float().cpu().numpy()
+    got_lse = lse.cpu().numpy()
+    qf = OL.bf16_to_f64(q).reshape(q.shape)
+    kf = OL.bf16_to_f64(kc).reshape(total, d)
+    vf = OL.bf16_to_f64(vc).reshape(total, d)
+    Ks = [kf[o // d:o // d + c][None] for o, c in zip(kv_off, caps)]
+    Vs = [vf[o // d:o // d + c][None] for o, c in zip(kv_off, caps)]
+    ref = OA.tree_attention(qf, Ks, Vs, ctxs, ns, row_off, mask, scale)
+    for (b, i), (o, lv) in ref.items():
+        rr = int(row_off[b]) + i
+        elem_ok, row_ok, e, ratio = row_errors(got[rr].astype(np.float64), o)
+        assert elem_ok and row_ok, (b, i, e, ratio)
+        assert lse_ok(got_lse[rr], lv), (b, i)
+
+
 def test_attention_skips_invalid_requests_in_the_sequence(api):
     """Requests skipped as invalid (context above max_ctx) in the middle and
     at the ends of the batch hold no key chunks: the work of the others is
