@@ -152,8 +152,8 @@ def test_workspace_sizes(native):
     # by d + 2 floats) and B + 1 chunk offsets.  One row block of 16 rows per
     # wave while that keeps <= 2 row groups and < 256 units, else the fewest
     # groups; workgroups: a multiple of the units while there are <= 128 of
-    # them (each taking >= 2 chunks), else one per two chunks of the largest
-    # batch the bounds allow, at most 256
+    # them (each taking >= 8 chunks), else one per eight chunks of the
+    # largest batch the bounds allow, at most 256
     def attn_ws(B, Hq, Hkv, d, max_ctx, max_n):
         rows = max_n * (Hq // Hkv)
         rb = -(-rows // 16)
@@ -164,9 +164,9 @@ def test_workspace_sizes(native):
         nch = -(-(max_ctx + max_n) // 64)
         units = B * Hkv * groups
         if 2 * units <= 256:
-            nwg = units * max(1, min(256 // units, nch // 2))
+            nwg = units * max(1, min(256 // units, nch // 8))
         else:
-            nwg = -(-(units * nch) // 2)
+            nwg = -(-(units * nch) // 8)
         nwg = max(1, min(256, nwg))
         return 2 * nwg * min(rb * 16, per_wg) * (d + 2) * 4 + (B + 1) * 4
 
@@ -176,8 +176,8 @@ def test_workspace_sizes(native):
     # worked by hand: 30 rows, 2 units of 2 chunks, one workgroup each
     assert attn_ws(1, 4, 2, 64, 100, 15) == 2 * 2 * 32 * 66 * 4 + 8
     # one request at 4K context, 240 rows: 2 row groups of 128 x 8 KV heads
-    # = 16 units of 65 chunks, 16 workgroups each
-    assert attn_ws(1, 32, 8, 128, 4096, 60) == 2 * 256 * 128 * 130 * 4 + 8
+    # = 16 units of 65 chunks, 8 workgroups each
+    assert attn_ws(1, 32, 8, 128, 4096, 60) == 2 * 128 * 128 * 130 * 4 + 8
     assert L.graft_tree_attention_workspace_bytes(0, 32, 8, 128, 4096, 60) == 0
 
 
