@@ -220,7 +220,10 @@ def test_lmhead_packed_equals_rowmajor(api, M, H, V):
                                      (68, 1024, 5000, 8), (65, 256, 130, 16), (960, 512, 4001, 8),
                                      (129, 256, 777, 10), (200, 128, 257, 16), (384, 128, 1023, 8),
                                      (4200, 128, 300, 8), (65, 128, 1, 1), (100, 128, 60, 1), (256, 256, 511, 3),
-                                     (257, 128, 129, 16)])
+                                     (257, 128, 129, 16),
+                                     # more than 32 m tiles of 256 rows (streams = 256 / tiles), up to the
+                                     # largest M the fused path takes
+                                     (8450, 128, 300, 8), (16384, 128, 260, 16)])
 def test_fused_packed_topk_equals_split(api, M, H, V, k):
     """Packed fused top-k (lists kept per workgroup across tiles) ranks
     exactly the logits the split row-major mode writes.  Up to 64 rows one
