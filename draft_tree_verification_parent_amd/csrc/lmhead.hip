@@ -979,7 +979,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(int M, int H, int V,
   constexpr int CW = 32;                 // vocabulary columns per epilogue pass
   constexpr int TSTR = CW + 4;           // floats per staged logit row
   static_assert(128 * TSTR * 4 <= WB && 128 * TSTR * 4 <= HB, "half a pass fits in a stage");
-  static_assert(WI == VB && HI == VB, "one W and one hidden DMA per vocabulary block");
+  static_assert(WI == VB && HI == VB && MB == VB, "two fragment reads and one DMA per MFMA group");
   static_assert(NW * WB + NH * HB <= 160 * 1024, "the rings fit in 160 KB of LDS");
   __shared__ __attribute__((aligned(1024))) unsigned char sm[NW * WB + NH * HB];
   unsigned char *const sw = sm;
@@ -1056,16 +1056,43 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(int M, int H, int V,
   F64Keys<K> list;  // hidden row m0 + tid
   list.init();
 
-  // prologue, in the order the waits below assume: W_0, H_0, W_1
+  // Ring schedule.  Chunk j's W sits in W stage j % 3 and its hidden rows in
+  // hidden stage j % 2.  The chunk's one barrier, B_j, sits between its two
+  // k-steps: the second k-step's fragments are read during the first, so
+  // at B_j every wave holds them in registers (chunk j's stages are no
+  // longer read) and no MFMA after the barrier waits on LDS; B_j also makes
+  // sure chunk j + 1 has landed.  The DMAs go eight per k-step, one per
+  // group of 8 MFMAs: W_j+2 in chunk j's first k-step (into the stage chunk
+  // j - 1 left at B_j-1), H_j+2 in its second (into chunk j's own hidden
+  // stage); both must land by B_j+1.  Issued evenly, the
+  // copies do not queue up behind each other in the address unit, which
+  // would stall the issuing wave and with it the MFMAs.  A tile's last
+  // chunk leaves its stages to the epilogue, which stages the tile's logits
+  // there and then issues that chunk's H_j+2.
+  //
+  // Prologue, in the order the waits assume: W_0, H_0, W_1, H_1; the first
+  // chunk's data must land before anything is read.
   if (Q > 0) {
-    const Dma w0 = w_dma(0), h0 = h_dma(0), w1 = w_dma(1);
+    const Dma w0 = w_dma(0), h0 = h_dma(0), w1 = w_dma(1), h1 = h_dma(1);
 #pragma unroll
     for (int i = 0; i < WI; ++i) lds_dma16_cached(w0.dst + i * 1024, w0.src, wo[i]);
 #pragma unroll
     for (int i = 0; i < HI; ++i) lds_dma16_cached(h0.dst + i * 1024, h0.src, ho[i]);
 #pragma unroll
     for (int i = 0; i < WI; ++i) lds_dma16_cached(w1.dst + i * 1024, w1.src, wo[i]);
+#pragma unroll
+    for (int i = 0; i < HI; ++i) lds_dma16_cached(h1.dst + i * 1024, h1.src, ho[i]);
+    ring_barrier<WI + HI>();  // W_0 and H_0 have landed, for every wave
   }
+  auto fw = [&](int j, int off) {
+    return *reinterpret_cast<const bf16x8 *>(sw + (j % NW) * WB + off);
+  };
+  auto fh = [&](int j, int off) {
+    return *reinterpret_cast<const bf16x8 *>(sh + (j % NH) * HB + off);
+  };
+  // fragments of the k-step in use (a: vocabulary, b: hidden) and of the
+  // next one, being read
+  bf16x8 a0[VB], b0[MB], a1[VB], b1[MB];
   int q = 0;
   for (int item = 0; item < items; ++item) {
     f32x4 acc[VB][MB];
@@ -1073,61 +1100,54 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(int M, int H, int V,
     for (int a = 0; a < VB; ++a)
 #pragma unroll
       for (int b = 0; b < MB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // Both k-steps of a chunk in one straight run; each vocabulary fragment
-    // is read one block ahead of its MFMAs, and k-step 1's hidden fragments
-    // during k-step 0.  (The next chunks' DMAs are issued before, not among,
-    // the MFMAs: code paths that branch between MFMA groups make the
-    // register allocator move the 256 accumulators at every block edge.)
-    // The next chunks' DMAs (H_q+1 during k-step 0, W_q+2 during k-step 1)
-    // go one per vocabulary block among the MFMAs, so the memory pipeline
-    // takes them while the MFMAs run instead of stalling the wave at issue.
-    auto chunk = [&](const unsigned char *stw, const unsigned char *sth, const Dma hn, const Dma wn) {
-      auto fw = [&](int off) { return *reinterpret_cast<const bf16x8 *>(stw + off); };
-      auto fh = [&](int off) { return *reinterpret_cast<const bf16x8 *>(sth + off); };
-      // the first MFMA needs only the first vocabulary fragment and the
-      // first hidden one: those are read first
-      bf16x8 b0[MB], b1[MB];
-      bf16x8 a = fw(fa[0]);
+    // One chunk, both k-steps in one straight run (code paths that branch
+    // between MFMA groups make the register allocator move the 256
+    // accumulators at every block edge; for the same reason no fragment is
+    // carried from one chunk to the next).  The first k-step's fragments
+    // are read at the top, in the order its first groups use them; in each
+    // group of the first k-step two fragments of the second are read (the
+    // hidden ones first: every group needs all of them).
+    auto chunk = [&](auto last_tag, int j) {
+      constexpr bool LAST = decltype(last_tag)::value;
+      a0[0] = fw(j, fa[0]);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) b0[mb] = fh(fb[0] + mb * 2048);
+      for (int mb = 0; mb < MB; ++mb) b0[mb] = fh(j, fb[0] + mb * 2048);
+#pragma unroll
+      for (int vb = 1; vb < VB; ++vb) a0[vb] = fw(j, fa[0] + vb * 2048);
       __builtin_amdgcn_sched_barrier(0);
-      // the hidden rows of the next chunk have one chunk of lead time: all
-      // at once, first
-#pragma unroll
-      for (int i = 0; i < HI; ++i) lds_dma16_cached(hn.dst + i * 1024, hn.src, ho[i]);
+      const Dma wn = w_dma(j + 2);
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
-        const bf16x8 an = vb + 1 < VB ? fw(fa[0] + (vb + 1) * 2048) : fw(fa[1]);
-        if (vb == VB / 2) {
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) b1[mb] = fh(fb[1] + mb * 2048);
+        if (vb < VB / 2) {
+          b1[2 * vb] = fh(j, fb[1] + 2 * vb * 2048);
+          b1[2 * vb + 1] = fh(j, fb[1] + (2 * vb + 1) * 2048);
+        } else {
+          a1[2 * vb - VB] = fw(j, fa[1] + (2 * vb - VB) * 2048);
+          a1[2 * vb - VB + 1] = fw(j, fa[1] + (2 * vb - VB + 1) * 2048);
         }
-        if (vb & 1) lds_dma16_cached(wn.dst + (vb >> 1) * 1024, wn.src, wo[vb >> 1]);
+        lds_dma16_cached(wn.dst + vb * 1024, wn.src, wo[vb]);
         __builtin_amdgcn_sched_barrier(0);  // the reads stay ahead of these MFMAs
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          acc[vb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0[mb], acc[vb][mb], 0, 0, 0);
-        a = an;
+          acc[vb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[vb], b0[mb], acc[vb][mb], 0, 0, 0);
       }
+      // B_j: this wave's reads of chunk j are done and, with W_j+2 (the
+      // youngest DMAs) still allowed in flight, W_j+1 and H_j+1 have landed
+      ring_barrier<WI>();
+      Dma hn{nullptr, 0u};
+      if constexpr (!LAST) hn = h_dma(j + 2);
 #pragma unroll
       for (int vb = 0; vb < VB; ++vb) {
-        bf16x8 an = a;
-        if (vb + 1 < VB) an = fw(fa[1] + (vb + 1) * 2048);
-        if (vb & 1) lds_dma16_cached(wn.dst + (4 + (vb >> 1)) * 1024, wn.src, wo[4 + (vb >> 1)]);
+        if constexpr (!LAST) lds_dma16_cached(hn.dst + vb * 1024, hn.src, ho[vb]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          acc[vb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1[mb], acc[vb][mb], 0, 0, 0);
-        a = an;
+          acc[vb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[vb], b1[mb], acc[vb][mb], 0, 0, 0);
       }
     };
-    for (int kc = 0; kc < nkc; ++kc, ++q) {
-      // W_q and H_q have landed once only W_q+1 (issued after H_q) may be
-      // in flight; the barrier also ends every wave's reads of chunk q - 1,
-      // whose stages H_q+1 and W_q+2 now fill
-      ring_barrier<WI>();
-      chunk(sw + (q % NW) * WB, sh + (q % NH) * HB, h_dma(q + 1), w_dma(q + 2));
-    }
+    for (int kc = 0; kc + 1 < nkc; ++kc, ++q) chunk(std::false_type{}, q);
+    chunk(std::true_type{}, q);
+    ++q;
 
     // ---- tile done: its logits go through the last chunk's two stages
     // (rows 0-127 in the W stage, 128-255 in the hidden stage) in passes of
@@ -1225,6 +1245,14 @@ __global__ __launch_bounds__(256, 1) void lmhead_big_kernel(int M, int H, int V,
         list.insert(key);
       }
       __syncthreads();  // the next pass overwrites the staged rows
+    }
+    // the staging stages are free again: the hidden rows two chunks after
+    // the tile's last one (q - 1) go into its hidden stage (W of the chunk
+    // after them goes into its W stage during the next chunk)
+    if (item + 1 < items) {
+      const Dma hn = h_dma(q + 1);
+#pragma unroll
+      for (int i = 0; i < HI; ++i) lds_dma16_cached(hn.dst + i * 1024, hn.src, ho[i]);
     }
   }
   // the DMAs past the last chunk must land before the workgroup ends
