@@ -892,21 +892,19 @@ __global__ __launch_bounds__(256, 1) void lmhead_wide_kernel(int M, int H, int V
 // ------------------------------------------------ packed W, 256 x 256 tiles
 // Past 128 hidden rows every byte a CU takes in is worth more flops with a
 // bigger tile: a 256 x 256 tile (hidden rows x vocabulary rows) feeds 128
-// flops per byte taken in against the 128 x 256 tile's 85, and the CU's
-// intake rate (30-35 GB/s once HBM misses share its request stream) is what
-// bounds this product.  4 wavefronts, each a 128 x 128 block (2 x 2 layout):
-// 64 accumulator tiles (256 accumulation registers) and 8 + 8 fragments per
-// k-step, read as in the 128-row kernel from 128-byte LDS rows swizzled by
-// (r % 8).
+// flops per byte taken in against the 128 x 256 tile's 85.  4 wavefronts,
+// each a 128 x 128 block (2 x 2 layout): 64 accumulator tiles (256
+// accumulation registers) and 8 + 8 fragments per k-step, read as in the
+// 128-row kernel from 128-byte LDS rows swizzled by (r % 8).
 //
 // A chunk is 64 hidden columns: 32 KB of W (two packed images) and 32 KB of
 // hidden rows.  W goes through a ring of three stages and the hidden rows
-// through a ring of two (160 KB in all), so that, while chunk q is
-// computed, W of chunks q + 1 and q + 2 and the hidden rows of chunk q + 1
-// are in flight: 96 KB, and the memory pipe never drains between chunks.
-// At the top of chunk q the wave waits for W_q and H_q (issued before W_q+1,
-// which may stay in flight); H_q+1 and W_q+2 go into the stages chunk q - 1
-// used, one DMA among each group of 8 MFMAs.
+// through a ring of two (160 KB in all).  What bounds the loop besides the
+// MFMAs is the number of copy instructions, not their bytes: copies of 4
+// bytes per lane instead of 16 take as long, and the copies cost about a
+// fifth of the kernel's time even when no wait for them remains, so they
+// are issued one per group of 8 MFMAs, never in bursts (the schedule is
+// described at the ring below).
 //
 // Epilogue (per tile): one thread per hidden row keeps one persistent sorted
 // list of k keys.  The tile's logits pass through the chunk's two consumed
