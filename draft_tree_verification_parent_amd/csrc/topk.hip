@@ -70,10 +70,21 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
     constexpr int B = kThreads * 4 * U;
     int base = lo;
     float bf = __uint_as_float(0xFFFFFFFFu);  // the value of order 0: a NaN
-    for (; base + B <= hi; base += B) {
-      float4 x[U];
+    // The next batch's loads are issued before this batch is screened, so
+    // each workgroup always has a batch in flight.
+    float4 x[U], xn[U];
+    if (base + B <= hi) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) x[u] = *reinterpret_cast<const float4 *>(row + base + (u * kThreads + tid) * 4);
+      for (int u = 0; u < U; ++u) xn[u] = *reinterpret_cast<const float4 *>(row + base + (u * kThreads + tid) * 4);
+    }
+    for (; base + B <= hi; base += B) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) x[u] = xn[u];
+      if (base + 2 * B <= hi) {  // uniform
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          xn[u] = *reinterpret_cast<const float4 *>(row + base + B + (u * kThreads + tid) * 4);
+      }
       if (base == lo) {
         // first batch (uniform): the K-th largest of the 64 lane maxima, so
         // the first inserts are already filtered
