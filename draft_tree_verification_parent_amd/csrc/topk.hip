@@ -30,6 +30,14 @@ constexpr int kSliceQuantum = 4;  // slices start on 16-byte boundaries
 
 using graft::TopKeys;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Four logits (16 bytes) read once: a non-temporal load (the logits are not read again,
+// and the stream runs at 0.77 of HBM peak this way against 0.70 cached).
+__device__ inline float4 load_stream4(const float *p) {
+  const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+  return make_float4(t[0], t[1], t[2], t[3]);
+}
+
 template <int K>
 __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__restrict__ logits, int V, int k,
                                                               int slice_len, uint64_t *__restrict__ part,
@@ -75,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
     float4 x[U], xn[U];
     if (base + B <= hi) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) xn[u] = *reinterpret_cast<const float4 *>(row + base + (u * kThreads + tid) * 4);
+      for (int u = 0; u < U; ++u) xn[u] = load_stream4(row + base + (u * kThreads + tid) * 4);
     }
     for (; base + B <= hi; base += B) {
 #pragma unroll
@@ -83,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
       if (base + 2 * B <= hi) {  // uniform
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          xn[u] = *reinterpret_cast<const float4 *>(row + base + B + (u * kThreads + tid) * 4);
+          xn[u] = load_stream4(row + base + B + (u * kThreads + tid) * 4);
       }
       if (base == lo) {
         // first batch (uniform): the K-th largest of the 64 lane maxima, so
