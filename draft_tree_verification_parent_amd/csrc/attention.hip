@@ -779,8 +779,9 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int max_n) {
   // Row blocks per wavefront.  With few (request, KV head) units a
   // workgroup's time is dominated by its fixed costs (first loads, partial
   // write) and lighter workgroups win (measured: 240 rows of one request at
-  // 4K context, 28 us with one block per wave in two row groups against 36
-  // with two), so one block per wave is used while that makes at most two
+  // 4K context, 23 us with one block per wave in two row groups against 32
+  // with two blocks in one, which reads the K/V once), so one block per wave
+  // is used while that makes at most two
   // row groups and fewer than 256 units; otherwise the fewest row groups
   // (each re-reads the unit's K/V), up to 3 blocks per wave (4 spill at
   // d = 128).
