@@ -781,10 +781,9 @@ Plan make_plan(int B, int Hq, int Hkv, int d, int max_ctx, int max_n) {
   // write) and lighter workgroups win (measured: 240 rows of one request at
   // 4K context, 23 us with one block per wave in two row groups against 32
   // with two blocks in one, which reads the K/V once), so one block per wave
-  // is used while that makes at most two
-  // row groups and fewer than 256 units; otherwise the fewest row groups
-  // (each re-reads the unit's K/V), up to 3 blocks per wave (4 spill at
-  // d = 128).
+  // is used while that makes at most two row groups and fewer than 256
+  // units; otherwise the fewest row groups (each re-reads the unit's K/V),
+  // up to 3 blocks per wave (4 spill at d = 128).
   const int rg1 = (rows + kWaves * 16 - 1) / (kWaves * 16);
   if (rg1 <= 2 && static_cast<long long>(B) * Hkv * rg1 < 256) p.rbw = 1;
   else p.rbw = rb <= kWaves ? 1 : rb <= 2 * kWaves ? 2 : 3;
