@@ -56,6 +56,12 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
 
   TopKeys<K> L;
   L.init();
+  // Each wave's bound, published for the others: an entry below any wave's
+  // bound is below K entries of the row, so every wave screens with the
+  // largest published one (a stale value is still a valid bound).
+  __shared__ uint32_t s_bound[4];
+  if (tid < 4) s_bound[tid] = 0;
+  __syncthreads();
   // An entry below a value that K distinct entries of the wave reach cannot
   // be in the top k <= K.  `bound` (a value order) is the K-th largest of the
   // 64 lanes' list heads after each batch, and of the lanes' maxima before
@@ -108,6 +114,14 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
         }
         bound = graft::wave_kth_u32<K>(lm);
         bf = graft::key_value(static_cast<uint64_t>(bound) << 32);
+        if (lane == 0) s_bound[wave] = bound;
+      }
+      {
+        const uint32_t ob = max(max(s_bound[0], s_bound[1]), max(s_bound[2], s_bound[3]));
+        if (ob > bound) {
+          bound = ob;
+          bf = graft::key_value(static_cast<uint64_t>(bound) << 32);
+        }
       }
       float mx = fmaxf(fmaxf(x[0].x, x[0].y), fmaxf(x[0].z, x[0].w));
 #pragma unroll
@@ -129,6 +143,7 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
       if (lb > bound) {
         bound = lb;
         bf = graft::key_value(static_cast<uint64_t>(bound) << 32);
+        if (lane == 0) s_bound[wave] = bound;
       }
     }
     // the partial batch at the end of the slice, entry by entry
