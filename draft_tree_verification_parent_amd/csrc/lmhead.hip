@@ -913,50 +913,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_wide_kernel(int M, int H, int V
 // against its own k-th key.  One list per (row, workgroup) is written at the
 // end and merged by topk_merge_kernel.  The MFMA sums run in the k-order of
 // every other path, so the logits are bit-identical.
-// A sorted list of K (value, id) keys whose compare-exchanges are two
-// fp64 instructions.  Key bits: order(value) << 30 | (2^30 - 1 - id): the
-// top two bits are clear, so as an fp64 bit pattern every key is a finite
-// non-negative number (subnormal for the smallest orders; fp64 subnormals
-// are not flushed) and fp64 order equals the integer order of the bits, the
-// (value desc, id asc) ranking.  0.0 is the empty slot.  Ids below 2^30 - 1.
-template <int K>
-struct F64Keys {
-  double k[K];
-  __device__ void init() {
-#pragma unroll
-    for (int j = 0; j < K; ++j) k[j] = 0.0;
-  }
-  __device__ static double make(float v, int id) {
-    const uint64_t bits = (static_cast<uint64_t>(graft::float_order(v)) << 30) |
-                          static_cast<uint64_t>((1u << 30) - 1u - static_cast<uint32_t>(id));
-    return __longlong_as_double(static_cast<long long>(bits));
-  }
-  // the K-th key's value (-inf while the list has an empty slot)
-  __device__ float kth_value() const {
-    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(k[K - 1]));
-    return b == 0 ? -INFINITY : graft::key_value(static_cast<uint64_t>(static_cast<uint32_t>(b >> 30)) << 32);
-  }
-  // branch-free insertion: x bubbles down the descending list (0.0, the
-  // empty key, leaves it unchanged).  One v_max_f64 and one v_min_f64 per
-  // slot, written out: the library calls would add two canonicalising
-  // operations each, and no key is a NaN.
-  __device__ void insert(double x) {
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      double hi, lo;
-      asm("v_max_f64 %0, %2, %3\n\tv_min_f64 %1, %2, %3" : "=&v"(hi), "=&v"(lo) : "v"(k[j]), "v"(x));
-      k[j] = hi;
-      x = lo;
-    }
-  }
-  // the key of slot j in the rank_key format the merge reads (0 = empty)
-  __device__ uint64_t rank_key(int j) const {
-    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(k[j]));
-    if (b == 0) return 0;
-    const uint32_t id = (1u << 30) - 1u - static_cast<uint32_t>(b & ((1u << 30) - 1u));
-    return (static_cast<uint64_t>(static_cast<uint32_t>(b >> 30)) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - id);
-  }
-};
+using graft::F64Keys;
 
 constexpr int BG_BM = 256;  // hidden rows per tile
 constexpr int BG_BV = 256;  // vocabulary rows per tile
@@ -1326,7 +1283,7 @@ extern "C" int graft_lmhead_topk(int M, int H, int V, int k, const graft_bf16 *h
                                  int w_layout, float *logits, int32_t *topk_id, float *topk_val, void *ws,
                                  size_t ws_bytes, graft_stream stream) {
   using graft::fail;
-  if (M < 0 || V <= 0 || k < 0 || k > GRAFT_MAX_K || k > V)
+  if (M < 0 || V <= 0 || V > GRAFT_MAX_V || k < 0 || k > GRAFT_MAX_K || k > V)
     return fail(GRAFT_EINVAL, "lmhead_topk: M=%d V=%d k=%d", M, V, k);
   if (w_layout != GRAFT_W_ROWMAJOR && w_layout != GRAFT_W_PACKED)
     return fail(GRAFT_EINVAL, "lmhead_topk: unknown weight layout %d", w_layout);
@@ -1550,7 +1507,7 @@ extern "C" int graft_lmhead_topk_noalloc(int M, int H, int V, int k, const graft
                                          const graft_bf16 *w_packed, int32_t *topk_id, float *topk_val,
                                          graft_stream stream) {
   using graft::fail;
-  if (M < 0 || V <= 0 || k < 1 || k > GRAFT_MAX_K || k > V)
+  if (M < 0 || V <= 0 || V > GRAFT_MAX_V || k < 1 || k > GRAFT_MAX_K || k > V)
     return fail(GRAFT_EINVAL, "lmhead_topk_noalloc: M=%d V=%d k=%d", M, V, k);
   if (!hidden || !w_packed || !topk_id) return fail(GRAFT_EINVAL, "lmhead_topk_noalloc: NULL array");
   if (packed_tiles_m(M) > PK_GRID)

@@ -54,7 +54,9 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
   const int lo = s * slice_len;
   const int hi = lo + slice_len < V ? lo + slice_len : V;
 
-  TopKeys<K> L;
+  // one sorted list per lane, fp64 keys: an insert is K v_max_f64 /
+  // v_min_f64 pairs (ids below 2^30, which the host checks)
+  graft::F64Keys<K> L;
   L.init();
   // Each wave's bound, published for the others: an entry below any wave's
   // bound is below K entries of the row, so every wave screens with the
@@ -135,11 +137,11 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
         const float xs[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (!(xs[e] < bf)) L.insert(graft::rank_key(xs[e], c + e));
+          if (!(xs[e] < bf)) L.insert(graft::F64Keys<K>::make(xs[e], c + e));
       }
       // each lane's list head is its largest entry: K lanes hold an entry
       // at least the K-th largest head
-      const uint32_t lb = graft::wave_kth_u32<K>(static_cast<uint32_t>(L.k[0] >> 32));
+      const uint32_t lb = graft::wave_kth_u32<K>(L.head_order());
       if (lb > bound) {
         bound = lb;
         bf = graft::key_value(static_cast<uint64_t>(bound) << 32);
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
         const float xs[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (c + e < hi && graft::float_order(xs[e]) >= bound) L.insert(graft::rank_key(xs[e], c + e));
+          if (c + e < hi && graft::float_order(xs[e]) >= bound) L.insert(graft::F64Keys<K>::make(xs[e], c + e));
       }
     }
   } else {
@@ -177,16 +179,19 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = base + u * kThreads + tid;
-        if (c < hi && graft::float_order(x[u]) >= bound) L.insert(graft::rank_key(x[u], c));
+        if (c < hi && graft::float_order(x[u]) >= bound) L.insert(graft::F64Keys<K>::make(x[u], c));
       }
       // each lane's list head is its largest entry: K lanes hold an entry
       // at least the K-th largest head
-      const uint32_t lb = graft::wave_kth_u32<K>(static_cast<uint32_t>(L.k[0] >> 32));
+      const uint32_t lb = graft::wave_kth_u32<K>(L.head_order());
       bound = lb > bound ? lb : bound;
     }
   }
 
-  uint64_t r = graft::wave_extract<K>(L, k);
+  TopKeys<K> LK;  // the lane's list as rank keys
+#pragma unroll
+  for (int j = 0; j < K; ++j) LK.k[j] = L.rank_key(j);
+  uint64_t r = graft::wave_extract<K>(LK, k);
   if (lane < k) s_k[wave][lane] = r;
   __syncthreads();
   if (wave == 0) {

@@ -6,6 +6,7 @@
 // comes back as +0; the two compare equal).  Key 0 is the empty slot.
 #pragma once
 
+#include <cmath>
 #include <type_traits>
 
 #include "common.h"
@@ -43,6 +44,55 @@ struct TopKeys {
 #pragma unroll
     for (int j = 0; j < K - 1; ++j) k[j] = k[j + 1];
     k[K - 1] = 0;
+  }
+};
+
+// A sorted list of K (value, id) keys whose compare-exchanges are two
+// fp64 instructions.  Key bits: order(value) << 30 | (2^30 - 1 - id): the
+// top two bits are clear, so as an fp64 bit pattern every key is a finite
+// non-negative number (subnormal for the smallest orders; fp64 subnormals
+// are not flushed) and fp64 order equals the integer order of the bits, the
+// (value desc, id asc) ranking.  0.0 is the empty slot.  Ids below 2^30 - 1.
+template <int K>
+struct F64Keys {
+  double k[K];
+  __device__ void init() {
+#pragma unroll
+    for (int j = 0; j < K; ++j) k[j] = 0.0;
+  }
+  __device__ static double make(float v, int id) {
+    const uint64_t bits = (static_cast<uint64_t>(graft::float_order(v)) << 30) |
+                          static_cast<uint64_t>((1u << 30) - 1u - static_cast<uint32_t>(id));
+    return __longlong_as_double(static_cast<long long>(bits));
+  }
+  // the K-th key's value (-inf while the list has an empty slot)
+  __device__ float kth_value() const {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(k[K - 1]));
+    return b == 0 ? -INFINITY : graft::key_value(static_cast<uint64_t>(static_cast<uint32_t>(b >> 30)) << 32);
+  }
+  // branch-free insertion: x bubbles down the descending list (0.0, the
+  // empty key, leaves it unchanged).  One v_max_f64 and one v_min_f64 per
+  // slot, written out: the library calls would add two canonicalising
+  // operations each, and no key is a NaN.
+  __device__ void insert(double x) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      double hi, lo;
+      asm("v_max_f64 %0, %2, %3\n\tv_min_f64 %1, %2, %3" : "=&v"(hi), "=&v"(lo) : "v"(k[j]), "v"(x));
+      k[j] = hi;
+      x = lo;
+    }
+  }
+  // the order of the head (largest) key's value, 0 while the list is empty
+  __device__ uint32_t head_order() const {
+    return static_cast<uint32_t>(static_cast<uint64_t>(__double_as_longlong(k[0])) >> 30);
+  }
+  // the key of slot j in the rank_key format the merge reads (0 = empty)
+  __device__ uint64_t rank_key(int j) const {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(k[j]));
+    if (b == 0) return 0;
+    const uint32_t id = (1u << 30) - 1u - static_cast<uint32_t>(b & ((1u << 30) - 1u));
+    return (static_cast<uint64_t>(static_cast<uint32_t>(b >> 30)) << 32) | static_cast<uint64_t>(0xFFFFFFFFu - id);
   }
 };
 

@@ -73,6 +73,9 @@ typedef void *graft_stream;
 
 #define GRAFT_MAX_NODES 64
 #define GRAFT_MAX_K 16
+/* Largest vocabulary the top-k paths take: their sort keys hold a token id
+ * in 30 bits. */
+#define GRAFT_MAX_V ((1 << 30) - 1)
 #define GRAFT_MAX_CAND 2048
 #define GRAFT_MAX_UPDATE_ROWS 4096
 #define GRAFT_MAX_TEMPLATE_ROWS 4096
@@ -349,7 +352,7 @@ int graft_tree_attention(int B, int Hq, int Hkv, int d, float scale,
  *                                            logits, which never reach
  *                                            memory (the serving mode)
  * The logits, and so the top-k, are bit-identical for both layouts and
- * all modes.  1 <= k <= min(GRAFT_MAX_K, V) when k is used.
+ * all modes.  1 <= k <= min(GRAFT_MAX_K, V) when k is used; V <= GRAFT_MAX_V.
  * ws (device): graft_lmhead_topk_workspace_bytes(M, V, k) bytes (enough
  * for every mode and layout).
  */

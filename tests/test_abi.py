@@ -82,6 +82,8 @@ def test_host_argument_validation_launches_nothing(native):
     assert L.graft_lmhead_topk(4, 256, 100, 4, 1, 1, 7, None, 1, None, 1, 1 << 20, None) == E
     assert L.graft_lmhead_topk(4, 192, 100, 4, 1, 1, 1, None, 1, None, 1, 1 << 20, None) == E
     assert L.graft_lmhead_topk(17000, 256, 100, 4, 1, 1, 1, None, 1, None, 1, 1 << 30, None) == E
+    # vocabularies past 2^30 - 1 ids (the sort keys hold an id in 30 bits)
+    assert L.graft_lmhead_topk(4, 0, 1 << 30, 4, None, None, 0, 1, 1, None, 1, 1 << 40, None) == E
     assert L.graft_lmhead_pack(100, 192, 1, 1, None) == E
     assert L.graft_lmhead_pack(100, 256, None, 1, None) == E
     # attention
