@@ -52,7 +52,7 @@ ERR_TOKEN, ERR_PARENT, ERR_NOT_CLOSED, ERR_CAPACITY, ERR_RANK, ERR_ALIGN = 1, 2,
 SRC_ROOT, SRC_DRAFT, SRC_RETRIEVED, SRC_REPLACED = 0, 1, 2, 3
 TREE_PRUNE, TREE_STATIC_REPLACE, TREE_TAIL = 0, 1, 2
 W_ROWMAJOR, W_PACKED = 0, 1
-MAX_NODES, MAX_K = 64, 16
+MAX_NODES, MAX_K, MAX_V = 64, 16, (1 << 30) - 1
 
 
 class GraftError(RuntimeError):
