@@ -116,10 +116,14 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
         }
         bound = graft::wave_kth_u32<K>(lm);
         bf = graft::key_value(static_cast<uint64_t>(bound) << 32);
-        if (lane == 0) s_bound[wave] = bound;
+        if (lane == 0) __hip_atomic_store(&s_bound[wave], bound, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
       {
-        const uint32_t ob = max(max(s_bound[0], s_bound[1]), max(s_bound[2], s_bound[3]));
+        // relaxed atomic loads: other waves store these meanwhile
+        uint32_t ob = 0;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2)
+          ob = max(ob, __hip_atomic_load(&s_bound[w2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
         if (ob > bound) {
           bound = ob;
           bf = graft::key_value(static_cast<uint64_t>(bound) << 32);
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
       if (lb > bound) {
         bound = lb;
         bf = graft::key_value(static_cast<uint64_t>(bound) << 32);
-        if (lane == 0) s_bound[wave] = bound;
+        if (lane == 0) __hip_atomic_store(&s_bound[wave], bound, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
     // the partial batch at the end of the slice, entry by entry
