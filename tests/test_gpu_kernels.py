@@ -72,6 +72,31 @@ def test_topk_matches_oracle(api, M, V, k):
     assert np.array_equal(vals.cpu().numpy(), ev)
 
 
+@pytest.mark.parametrize("M,V,k", [(300, 151936, 8), (300, 151936, 16), (4, 151936, 16), (3, 5003, 8)])
+def test_topk_ordered_and_one_sided_rows(api, M, V, k):
+    """Rows that stress the screening: increasing (every batch beats the
+    bound), decreasing (only the first batch matters), and rows whose large
+    entries all fall to the lanes of one wavefront of a workgroup (entry
+    index / 4 mod 256 in [192, 256)), so the other waves screen only with
+    the bound that wavefront publishes; checked against the oracle."""
+    say(f"[topk ordered] M={M} V={V} k={k}")
+    r = np.random.default_rng(M * 13 + V + k)
+    x = r.standard_normal((M, V)).astype(np.float32)
+    x[0] = np.arange(V, dtype=np.float32) * 1e-3
+    x[1] = -np.arange(V, dtype=np.float32) * 1e-3
+    one_wave = ((np.arange(V) // 4) % 256) >= 192
+    x[2:, one_wave] += 8.0
+    logits = torch.from_numpy(x).cuda()
+    ids = torch.empty(M, k, dtype=torch.int32, device="cuda")
+    vals = torch.empty(M, k, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(api.graft_lmhead_topk_workspace_bytes(M, V, k), 1), dtype=torch.uint8, device="cuda")
+    api.graft_lmhead_topk(M, 0, V, k, None, None, logits, ids, vals, ws)
+    torch.cuda.synchronize()
+    eid, ev = OT.topk(x, k)
+    assert np.array_equal(ids.cpu().numpy(), eid)
+    assert np.array_equal(vals.cpu().numpy(), ev)
+
+
 @pytest.mark.parametrize("M,V,k", [(4, 1000, 8), (3, 200000, 10), (2, 9, 8)])
 def test_topk_nan_ranks_last(api, M, V, k):
     """NaN logits rank below every number (-inf included) and tie with each
