@@ -368,7 +368,8 @@ int graft_lmhead_topk(int M, int H, int V, int k,
  * graft_lmhead_topk without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): the fused packed mode (hidden given,
- * logits not materialised, w_packed from graft_lmhead_pack, H % 128 == 0)
+ * logits not materialised, w_packed from graft_lmhead_pack, H % 128 == 0,
+ * 1 <= k <= min(GRAFT_MAX_K, V), V <= GRAFT_MAX_V)
  * with its scratch (the per-(row, workgroup) candidate lists) in an array
  * built into the library, GRAFT_NOALLOC_SCRATCH_BYTES per GPU, held until the
  * process ends.  graft_lmhead_topk_noalloc_bytes(M, k) is the scratch a call
