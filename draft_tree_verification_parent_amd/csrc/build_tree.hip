@@ -25,6 +25,7 @@
 // static replacement looks up the table in rounds, one per link of the
 // longest chain of replaced nodes.
 #include "common.h"
+#include "topk_list.h"
 
 namespace {
 
@@ -44,33 +45,7 @@ __device__ void write_padding(int from, int to, int32_t *parent, int32_t *token,
   }
 }
 
-// Value of the lane whose index differs from this lane's in bit J, without
-// LDS traffic: DPP quad permutes (J = 1, 2), DPP row rotates (J = 4, 8;
-// lane i reads lane i - N mod 16 under a rotate by N) and the gfx950
-// row-swap permutes (J = 16, 32), which hand back the even and the odd
-// half of each pair of rows.
-template <int J>
-__device__ inline uint32_t lane_xor32(uint32_t x, int lane) {
-  const int v = static_cast<int>(x);
-  if constexpr (J == 1) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
-  } else if constexpr (J == 2) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
-  } else if constexpr (J == 4) {
-    const int up = __builtin_amdgcn_update_dpp(0, v, 0x12C, 0xF, 0xF, false);  // lane i + 4
-    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // lane i - 4
-    return static_cast<uint32_t>((lane & 4) ? dn : up);
-  } else if constexpr (J == 8) {
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
-  } else if constexpr (J == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return (lane & 16) ? r[0] : r[1];
-  } else {
-    static_assert(J == 32, "lane distance 1..32");
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return (lane & 32) ? r[0] : r[1];
-  }
-}
+using graft::lane_xor32;
 
 template <int J>
 __device__ inline uint64_t lane_xor(uint64_t x, int lane) {

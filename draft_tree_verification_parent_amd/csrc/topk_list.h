@@ -155,19 +155,73 @@ __device__ inline uint32_t wave_max_u32(uint32_t x) {
   return mx(b[0], b[1]);
 }
 
-// The K-th largest of the 64 lanes' values (0 = none): K rounds of
-// remove-the-largest; lanes holding an equal maximum are removed together,
-// which only lowers the result.
+// Value of the lane whose index differs from this lane's in bit J, without
+// LDS traffic: DPP quad permutes (J = 1, 2), DPP row rotates (J = 4, 8;
+// lane i reads lane i - N mod 16 under a rotate by N) and the gfx950
+// row-swap permutes (J = 16, 32), which hand back the even and the odd
+// half of each pair of rows.
+template <int J>
+__device__ inline uint32_t lane_xor32(uint32_t x, int lane) {
+  const int v = static_cast<int>(x);
+  if constexpr (J == 1) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));
+  } else if constexpr (J == 2) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));
+  } else if constexpr (J == 4) {
+    const int up = __builtin_amdgcn_update_dpp(0, v, 0x12C, 0xF, 0xF, false);  // lane i + 4
+    const int dn = __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // lane i - 4
+    return static_cast<uint32_t>((lane & 4) ? dn : up);
+  } else if constexpr (J == 8) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false));
+  } else if constexpr (J == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    static_assert(J == 32, "lane distance 1..32");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+
+// The K-th largest of the 64 lanes' values (0 = none): a bitonic sort of the
+// 64 values, largest in lane 0, then lane K - 1's value, in 21 exchange
+// steps whatever K (K rounds of a wave-wide maximum cost about 7 per round).
 template <int K>
 __device__ inline uint32_t wave_kth_u32(uint32_t v) {
-  uint32_t kth = 0;
-#pragma unroll
-  for (int r = 0; r < K; ++r) {
-    const uint32_t b = wave_max_u32(v);
-    v = v == b ? 0u : v;
-    kth = b;
-  }
-  return kth;
+  static_assert(K >= 1 && K <= 64, "one value per lane");
+  const int lane = static_cast<int>(threadIdx.x & 63);
+  auto step = [&](auto k_tag, auto j_tag) {
+    constexpr int KB = decltype(k_tag)::value;
+    constexpr int J = decltype(j_tag)::value;
+    const uint32_t y = lane_xor32<J>(v, lane);
+    // descending overall: within blocks of KB whose bit KB is clear the
+    // lower lane of each pair keeps the larger value
+    const bool keep_max = ((lane & KB) == 0) == ((lane & J) == 0);
+    v = keep_max ? (v > y ? v : y) : (v < y ? v : y);
+  };
+  using std::integral_constant;
+  step(integral_constant<int, 2>{}, integral_constant<int, 1>{});
+  step(integral_constant<int, 4>{}, integral_constant<int, 2>{});
+  step(integral_constant<int, 4>{}, integral_constant<int, 1>{});
+  step(integral_constant<int, 8>{}, integral_constant<int, 4>{});
+  step(integral_constant<int, 8>{}, integral_constant<int, 2>{});
+  step(integral_constant<int, 8>{}, integral_constant<int, 1>{});
+  step(integral_constant<int, 16>{}, integral_constant<int, 8>{});
+  step(integral_constant<int, 16>{}, integral_constant<int, 4>{});
+  step(integral_constant<int, 16>{}, integral_constant<int, 2>{});
+  step(integral_constant<int, 16>{}, integral_constant<int, 1>{});
+  step(integral_constant<int, 32>{}, integral_constant<int, 16>{});
+  step(integral_constant<int, 32>{}, integral_constant<int, 8>{});
+  step(integral_constant<int, 32>{}, integral_constant<int, 4>{});
+  step(integral_constant<int, 32>{}, integral_constant<int, 2>{});
+  step(integral_constant<int, 32>{}, integral_constant<int, 1>{});
+  step(integral_constant<int, 64>{}, integral_constant<int, 32>{});
+  step(integral_constant<int, 64>{}, integral_constant<int, 16>{});
+  step(integral_constant<int, 64>{}, integral_constant<int, 8>{});
+  step(integral_constant<int, 64>{}, integral_constant<int, 4>{});
+  step(integral_constant<int, 64>{}, integral_constant<int, 2>{});
+  step(integral_constant<int, 64>{}, integral_constant<int, 1>{});
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), K - 1));
 }
 
 // Largest float over aligned groups of W <= 8 lanes (every lane of the group gets it).
