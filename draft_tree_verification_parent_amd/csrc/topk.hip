@@ -72,9 +72,9 @@ __global__ __launch_bounds__(kThreads) void topk_slice_kernel(const float *__res
   // 16 slots rarely run an insert.  (A uniform trip count keeps all 64 lanes
   // in the cross-lane max.)
   uint32_t bound = 0;
-  // 16-byte loads per thread per batch, issued together (the longer lists'
-  // larger per-batch bound update is spread over twice the entries)
-  constexpr int U = K <= 8 ? 4 : 8;
+  // 16-byte loads per thread per batch, issued together (8 for the longer
+  // lists measured slower once their bound update was a sort)
+  constexpr int U = 4;
   if ((V & 3) == 0) {
     // Whole batches need no bounds checks.  The screen is a float compare
     // against the bound's value, !(x < bf): for numbers it is order(x) >=
