@@ -248,7 +248,10 @@ def test_lmhead_packed_equals_rowmajor(api, M, H, V):
                                      (257, 128, 129, 16),
                                      # more than 32 m tiles of 256 rows (streams = 256 / tiles), up to the
                                      # largest M the fused path takes
-                                     (8450, 128, 300, 8), (16384, 128, 260, 16)])
+                                     (8450, 128, 300, 8), (16384, 128, 260, 16),
+                                     # more vocabulary tiles than tile streams: a round of whole 256 x
+                                     # 256 tiles per stream, then a partial round (4, 3 and 6 m tiles)
+                                     (960, 128, 20892, 8), (520, 128, 25500, 16), (1400, 128, 14300, 8)])
 def test_fused_packed_topk_equals_split(api, M, H, V, k):
     """Packed fused top-k (lists kept per workgroup across tiles) ranks
     exactly the logits the split row-major mode writes.  Up to 64 rows one
