@@ -212,7 +212,7 @@ def test_end_to_end_argmax_where_margin_is_clear(cfg, n_rows):
     say(f"[e2e] cfg {cfg}: {int(clear.sum())} of {len(rows)} rows have a clear margin; all match")
 
 
-@pytest.mark.parametrize("cfg,per_graph", [(1, 1), (2, 1), (2, 3)])
+@pytest.mark.parametrize("cfg,per_graph", [(1, 1), (2, 1), (2, 3), (5, 2)])
 def test_graph_replay_matches_eager(cfg, per_graph):
     """Rounds captured as a HIP graph (per_graph chained rounds in one graph)
     and replayed several times, with unrelated eager work and
