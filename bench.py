@@ -252,7 +252,10 @@ def measure(cfg, steps, warmup, with_cpu, extras):
     lm_s = step_us["lmhead_topk"] * 1e-6
     wide = M > 64
     kk = 8 if ri.k <= 8 else 16
-    kern = (f"lmhead_big_kernel<{kk}> + topk_merge_kernel<{kk}> (one graft_lmhead_topk call, packed weights, "
+    # the merge takes one wavefront per row when the lm-head leaves at most 64 lists per row (four or more 256-row
+    # m tiles)
+    merge = "topk_merge_wave_kernel" if M > 3 * 256 else "topk_merge_kernel"
+    kern = (f"lmhead_big_kernel<{kk}> + {merge}<{kk}> (one graft_lmhead_topk call, packed weights, "
             f"{M} rows, 256 x 256 tiles)" if M > 128 else
             f"lmhead_wide_kernel + topk_merge_kernel<{kk}> (one graft_lmhead_topk call, packed weights, {M} rows)"
             if wide else

@@ -268,6 +268,33 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(int S, int k, cons
   }
 }
 
+// At most 64 candidate lists per row (the lm-head kernels past 64 rows
+// write one per tile stream): one wavefront per row, four rows per
+// workgroup; lane t takes list t as its own and the wavefront extracts the
+// k best.  The same keys as topk_merge_kernel, whose other three
+// wavefronts would hold only empty lists.
+template <int K>
+__global__ __launch_bounds__(kThreads) void topk_merge_wave_kernel(int M, int S, int k,
+                                                                   const uint64_t *__restrict__ part,
+                                                                   int32_t *__restrict__ out_id,
+                                                                   float *__restrict__ out_val) {
+  const int m = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (m >= M) return;  // the whole wavefront
+  TopKeys<K> L;
+  L.init();
+  if (lane < S) {
+    const uint64_t *lst = part + (static_cast<size_t>(m) * S + lane) * k;
+#pragma unroll
+    for (int j = 0; j < K; ++j) L.k[j] = j < k ? lst[j] : 0;
+  }
+  const uint64_t r = graft::wave_extract<K>(L, k);
+  if (lane < k) {
+    out_id[static_cast<size_t>(m) * k + lane] = r ? graft::key_id(r) : 0;
+    if (out_val) out_val[static_cast<size_t>(m) * k + lane] = r ? graft::key_value(r) : -INFINITY;
+  }
+}
+
 // One draw per row at temperature T by the Gumbel-max identity on
 // materialised logits: argmax_t fl(fl(l_t * inv_temp) + g_t), ties to the
 // lower id, NaN below every number.  One 256-thread workgroup per row.
@@ -354,6 +381,16 @@ int launch_topk(int M, int V, int k, const float *logits, int32_t *topk_id, floa
 
 int launch_topk_merge(int M, int slices, int k, const uint64_t *part, int32_t *topk_id, float *topk_val,
                       hipStream_t stream) {
+  if (slices <= 64) {
+    const dim3 grid((M + kThreads / 64 - 1) / (kThreads / 64));
+    if (k <= 8)
+      hipLaunchKernelGGL(topk_merge_wave_kernel<8>, grid, dim3(kThreads), 0, stream, M, slices, k, part, topk_id,
+                         topk_val);
+    else
+      hipLaunchKernelGGL(topk_merge_wave_kernel<16>, grid, dim3(kThreads), 0, stream, M, slices, k, part, topk_id,
+                         topk_val);
+    return check_launch("topk merge");
+  }
   if (k <= 8)
     hipLaunchKernelGGL(topk_merge_kernel<8>, dim3(M), dim3(kThreads), 0, stream, slices, k, part, topk_id, topk_val);
   else
