@@ -25,7 +25,7 @@ def test_noalloc_equals_workspace_entry_point():
     from draft_tree_verification_parent_amd import api
     from draft_tree_verification_parent_amd._native import W_PACKED
 
-    # 960 rows (wide tiles, 128-row m tiles) then 60 rows (the 64-row kernel)
+    # 960 rows (256 x 256 tiles, four m tiles) then 60 rows (the 64-row kernel)
     for M, H, V, k, seed in ((960, 1024, 20011, 8, 1), (60, 512, 9000, 16, 2)):
         need = api.graft_lmhead_topk_noalloc_bytes(M, k)
         assert 0 < need <= api.graft_lmhead_topk_noalloc_bytes(16384, 16) <= 8 << 20
