@@ -268,10 +268,11 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(int S, int k, cons
   }
 }
 
-// At most 64 candidate lists per row (the lm-head kernels past 64 rows
-// write one per tile stream): one wavefront per row, four rows per
-// workgroup; lane t takes list t as its own and the wavefront extracts the
-// k best.  The same keys as topk_merge_kernel, whose other three
+// At most 64 candidate lists per row (a sliced top-k of a vocabulary up to
+// 64 x 4096 entries, and the 256 x 256 lm-head kernel from four m tiles on,
+// which writes one list per tile stream): one wavefront per row, four rows
+// per workgroup; lane t takes list t as its own and the wavefront extracts
+// the k best.  The same keys as topk_merge_kernel, whose other three
 // wavefronts would hold only empty lists.
 template <int K>
 __global__ __launch_bounds__(kThreads) void topk_merge_wave_kernel(int M, int S, int k,
@@ -349,9 +350,9 @@ TopkPlan topk_plan(int M, int V, int k) {
   // at least one workgroup per CU, slices of equal length (at least 4096
   // entries: a slice's first batch sets its bound).  Past 256 rows one
   // workgroup per row: more slices measured slower (960 x 151936 fp32
-  // logits, cold: 110 us with one slice per row, 119 with two, 121 with
-  // four; k = 16: 141, 174, 222), each adding its own bound set-up, list
-  // extraction and merge.
+  // logits, cold, with an earlier version of the slice kernel: 110 us with
+  // one slice per row, 119 with two, 121 with four; k = 16: 141, 174, 222),
+  // each adding its own bound set-up, list extraction and merge.
   const int max_slices = (V + 4095) / 4096;
   int want = M > 0 ? (256 + M - 1) / M : 1;
   if (want > max_slices) want = max_slices;
