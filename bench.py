@@ -45,7 +45,8 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16
 METRIC = "verify-round latency (µs) & verified tree tokens/s; % MFMA / HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_traffic.json")
-LMHEAD_SRC = os.path.join(ROOT, "draft_tree_verification_parent_amd", "csrc", "lmhead.hip")
+LMHEAD_SRCS = [os.path.join(ROOT, "draft_tree_verification_parent_amd", "csrc", n)
+               for n in ("lmhead.hip", "topk.hip", "topk_list.h")]
 CPU_SAMPLE_REQUESTS = 2  # requests of a batched workload the oracle is timed on
 
 
@@ -54,8 +55,14 @@ def log(msg):
 
 
 def lmhead_source_hash():
-    with open(LMHEAD_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """SHA-256 (first 16 hex digits) of the sources of one graft_lmhead_topk
+    call's kernels: the lm-head kernels, the top-k merge and their shared
+    key lists, read in that order."""
+    h = hashlib.sha256()
+    for path in LMHEAD_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload_key):

@@ -466,8 +466,10 @@ __global__ __launch_bounds__(PW * 64, 1) void lmhead_packed_kernel(int M, int H,
       }
       // SAMPLE: this row's noise is loaded first (16-byte loads while the
       // thread's 16 columns lie inside the row) and used only after the top-k
-      // work below, so waiting for it (which also waits for the ring's older
-      // DMAs) costs little.  Columns past V re-read column V - 1.
+      // work below.  The wait for it also waits for the ring's two newest
+      // chunks (the load counter is in order), once per tile: about 18 us of
+      // the 22 the draw adds at 60 rows x 128256.  Columns past V re-read
+      // column V - 1.
       float gv[SAMPLE ? VPT : 1];
       const int ms = m0 + row;
       if constexpr (SAMPLE) {
